@@ -1,0 +1,365 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each test names the fact it checks.  None of them re-types the oracle's formula:
+they use the page's worked example, a library routine (torch's fp64 scaled-dot-
+product attention and autograd), closed forms, invariants and finite differences.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sequence_parallelism_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _sdpa(q, k, v, mask=None, scale=None):
+    """torch fp64 SDPA on [S][H][D] numpy arrays, GQA by repeating kv heads."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+    tk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)[None]
+    tv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)[None]
+    m = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def _packed_pos(lengths):
+    return inputs.position_ids(lengths)
+
+
+# ---- the page's worked example (Ring Attention glossary, four-device simulation) ----
+
+def test_ring_example_matches_page():
+    g = json.load(open(os.path.join(GOLDEN, "ring_attention_example.json")))
+    q, k, v = inputs.ring_example()
+    assert tuple(q.shape) == (g["n_devices"] * g["block"], g["dim"])
+    raw = oracle.ring_sim_raw(q.numpy(), k.numpy(), v.numpy(), g["n_devices"])
+    full = oracle.full_attention_noncausal(q.numpy(), k.numpy(), v.numpy())
+    assert np.allclose(raw, full, atol=g["allclose_atol"]) == g["matches_full_attention"]
+    # in float64 the identity is exact up to rounding
+    assert np.max(np.abs(raw - full)) < 1e-12
+
+
+def test_ring_online_and_blockwise_equal_full_attention():
+    q, k, v = (t.numpy() for t in inputs.ring_example())
+    o_on, lse_on = oracle.ring_sim_online(q, k, v, 4)
+    o_full, lse_full = oracle.attention_fwd(q[:, None], k[:, None], v[:, None])
+    assert np.max(np.abs(o_on - o_full[:, 0])) < 1e-12
+    assert np.max(np.abs(lse_on - lse_full[0])) < 1e-12
+    # and agrees with the library's softmax attention
+    ref = _sdpa(q[:, None].astype(np.float64), k[:, None].astype(np.float64),
+                v[:, None].astype(np.float64))
+    assert np.max(np.abs(o_full - ref)) < 1e-12
+
+
+# ---- forward vs library routine ----
+
+@pytest.mark.parametrize("S,Hq,Hkv,D", [(37, 2, 2, 8), (64, 4, 1, 16), (50, 6, 2, 5)])
+def test_forward_matches_sdpa_noncausal(S, Hq, Hkv, D):
+    q, k, v = _rand((S, Hq, D), 1), _rand((S, Hkv, D), 2), _rand((S, Hkv, D), 3)
+    o, _ = oracle.attention_fwd(q, k, v)
+    assert np.max(np.abs(o - _sdpa(q, k, v))) < 1e-12
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,D,scale", [(41, 2, 1, 8, None), (64, 4, 2, 16, 0.3)])
+def test_forward_matches_sdpa_causal_single_doc(S, Hq, Hkv, D, scale):
+    q, k, v = _rand((S, Hq, D), 4), _rand((S, Hkv, D), 5), _rand((S, Hkv, D), 6)
+    pos = np.arange(S, dtype=np.int32)
+    o, _ = oracle.attention_fwd(q, k, v, pos=pos, causal=True, scale=scale)
+    tril = np.tril(np.ones((S, S), dtype=bool))
+    assert np.max(np.abs(o - _sdpa(q, k, v, mask=tril, scale=scale))) < 1e-12
+
+
+def test_forward_matches_sdpa_packed_docs_block_diagonal():
+    lengths = [5, 1, 9, 3, 14]
+    S = sum(lengths)
+    pos = _packed_pos(lengths)
+    q, k, v = _rand((S, 2, 8), 7), _rand((S, 2, 8), 8), _rand((S, 2, 8), 9)
+    o, _ = oracle.attention_fwd(q, k, v, pos=pos, causal=True)
+    mask = np.zeros((S, S), dtype=bool)
+    a = 0
+    for L in lengths:   # block-diagonal causal mask built from the lengths
+        mask[a:a + L, a:a + L] = np.tril(np.ones((L, L), dtype=bool))
+        a += L
+    assert np.max(np.abs(o - _sdpa(q, k, v, mask=mask))) < 1e-12
+
+
+# ---- invariants and closed forms ----
+
+def test_probability_rows_sum_to_one():
+    lengths = [7, 12, 1, 20]
+    S = sum(lengths)
+    q, k = _rand((S, 3, 8), 10) * 3, _rand((S, 3, 8), 11)
+    P = oracle.attention_probs(q, k, pos=_packed_pos(lengths), causal=True)
+    assert np.max(np.abs(P.sum(axis=-1) - 1.0)) < 1e-13
+    assert (P >= 0).all()
+
+
+def test_zero_query_gives_mean_of_visible_values_and_log_count():
+    lengths = [6, 11, 4]
+    S = sum(lengths)
+    pos = _packed_pos(lengths)
+    q = np.zeros((S, 2, 8))
+    k, v = _rand((S, 1, 8), 12), _rand((S, 1, 8), 13)
+    o, lse = oracle.attention_fwd(q, k, v, pos=pos, causal=True)
+    a = 0
+    for L in lengths:
+        for t in range(L):
+            mean = v[a:a + t + 1, 0].mean(axis=0)     # keys a..a+t are the visible ones
+            assert np.max(np.abs(o[a + t] - mean)) < 1e-14
+            assert np.allclose(lse[:, a + t], np.log(t + 1), atol=1e-14)
+        a += L
+
+
+def test_noncausal_invariant_to_joint_key_permutation():
+    q, k, v = _rand((30, 2, 8), 14), _rand((30, 2, 8), 15), _rand((30, 2, 8), 16)
+    perm = np.random.default_rng(17).permutation(30)
+    o1, l1 = oracle.attention_fwd(q, k, v)
+    o2, l2 = oracle.attention_fwd(q, k[perm], v[perm])
+    assert np.max(np.abs(o1 - o2)) < 1e-13 and np.max(np.abs(l1 - l2)) < 1e-13
+
+
+def test_packed_equals_per_document_attention():
+    lengths = [9, 3, 17]
+    S = sum(lengths)
+    pos = _packed_pos(lengths)
+    q, k, v = _rand((S, 4, 8), 18), _rand((S, 2, 8), 19), _rand((S, 2, 8), 20)
+    o, lse = oracle.attention_fwd(q, k, v, pos=pos, causal=True)
+    a = 0
+    for L in lengths:
+        od, ld = oracle.attention_fwd(q[a:a + L], k[a:a + L], v[a:a + L],
+                                      pos=np.arange(L, dtype=np.int32), causal=True)
+        assert np.max(np.abs(o[a:a + L] - od)) < 1e-13
+        assert np.max(np.abs(lse[:, a:a + L] - ld)) < 1e-13
+        a += L
+
+
+def test_future_keys_do_not_change_earlier_rows():
+    S = 40
+    pos = np.arange(S, dtype=np.int32)
+    q, k, v = _rand((S, 2, 8), 21), _rand((S, 1, 8), 22), _rand((S, 1, 8), 23)
+    o1, l1 = oracle.attention_fwd(q, k, v, pos=pos, causal=True)
+    k2, v2 = k.copy(), v.copy()
+    k2[25:] += 5.0
+    v2[25:] -= 3.0
+    o2, l2 = oracle.attention_fwd(q, k2, v2, pos=pos, causal=True)
+    assert np.array_equal(o1[:25], o2[:25]) and np.array_equal(l1[:, :25], l2[:, :25])
+    assert not np.allclose(o1[25:], o2[25:])
+
+
+def test_score_shift_changes_lse_only_even_for_huge_logits():
+    """Adding c to every score of every row (an extra q/k dimension carrying c)
+    leaves O unchanged and adds c to LSE; c = 1000 overflows a raw exponential,
+    so this pins the running-max subtraction of production kernels (Ring
+    Attention page, remark after the simulation)."""
+    S, D = 33, 8
+    pos = _packed_pos([10, 23])
+    q, k, v = _rand((S, 2, D), 24), _rand((S, 2, D), 25), _rand((S, 2, D), 26)
+    scale = 0.5
+    o1, l1 = oracle.attention_fwd(q, k, v, pos=pos, causal=True, scale=scale)
+    c = 1000.0
+    q2 = np.concatenate([q, np.full((S, 2, 1), c / scale)], axis=2)
+    k2 = np.concatenate([k, np.ones((S, 2, 1))], axis=2)
+    v2 = v
+    o2, l2 = oracle.attention_fwd(q2, k2, v2, pos=pos, causal=True, scale=scale)
+    assert np.all(np.isfinite(o2)) and np.all(np.isfinite(l2))
+    assert np.max(np.abs(o1 - o2)) < 1e-12
+    assert np.max(np.abs((l2 - l1) - c)) < 1e-9
+
+
+def test_rows_without_visible_keys_give_zero_and_minus_inf():
+    # query block entirely before the key block: nothing visible
+    S = 8
+    pos = np.arange(32, dtype=np.int32)
+    q, k, v = _rand((S, 1, 4), 27), _rand((S, 1, 4), 28), _rand((S, 1, 4), 29)
+    o, lse = oracle.attention_fwd(q, k, v, pos=pos, q_start=0, k_start=16, causal=True)
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+def test_sampled_rows_equal_full_evaluation():
+    lengths = [30, 50, 20]
+    S = sum(lengths)
+    pos = _packed_pos(lengths)
+    q, k, v = _rand((S, 4, 8), 30), _rand((S, 1, 8), 31), _rand((S, 1, 8), 32)
+    o, lse = oracle.attention_fwd(q, k, v, pos=pos, causal=True)
+    rows = np.array([0, 29, 30, 55, 99])
+    os_, ls_ = oracle.attention_fwd(q, k, v, pos=pos, causal=True, rows=rows)
+    assert np.array_equal(os_, o[rows]) and np.array_equal(ls_, lse[:, rows])
+
+
+# ---- merge ----
+
+def test_merge_of_disjoint_key_blocks_equals_attention_over_union():
+    S = 48
+    pos = _packed_pos([20, 28])
+    q, k, v = _rand((S, 2, 8), 33), _rand((S, 1, 8), 34), _rand((S, 1, 8), 35)
+    o_full, l_full = oracle.attention_fwd(q, k, v, pos=pos, causal=True)
+    # three key blocks, merged in ring order for each query block
+    cuts = [0, 13, 31, 48]
+    o_acc = np.zeros((S, 2, 8))
+    l_acc = np.full((2, S), -np.inf)
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        o_p, l_p = oracle.attention_fwd(q, k[a:b], v[a:b], pos=pos, k_start=a, causal=True)
+        o_acc, l_acc = oracle.lse_merge(o_acc, l_acc, o_p, l_p)
+    assert np.max(np.abs(o_acc - o_full)) < 1e-13
+    assert np.max(np.abs(l_acc - l_full)) < 1e-13
+
+
+def test_merge_identity_and_commutativity():
+    o = _rand((10, 2, 4), 36)
+    l = _rand((2, 10), 37)
+    z, zl = np.zeros_like(o), np.full_like(l, -np.inf)
+    m1, n1 = oracle.lse_merge(o, l, z, zl)
+    assert np.array_equal(m1, o) and np.allclose(n1, l, atol=1e-15)
+    m2, n2 = oracle.lse_merge(z, zl, z, zl)
+    assert np.all(m2 == 0) and np.all(n2 == -np.inf)
+    o2, l2 = _rand((10, 2, 4), 38), _rand((2, 10), 39)
+    a, b = oracle.lse_merge(o, l, o2, l2)
+    c, d = oracle.lse_merge(o2, l2, o, l)
+    assert np.max(np.abs(a - c)) < 1e-15 and np.max(np.abs(b - d)) < 1e-15
+
+
+# ---- backward ----
+
+def _loss(q, k, v, do, **kw):
+    o, _ = oracle.attention_fwd(q, k, v, threads=1, **kw)
+    return float(np.sum(o * do))
+
+
+def test_backward_matches_central_finite_differences():
+    lengths = [5, 7]
+    S = sum(lengths)
+    pos = _packed_pos(lengths)
+    kw = dict(pos=pos, causal=True, scale=0.7)
+    q, k, v = _rand((S, 2, 4), 40), _rand((S, 1, 4), 41), _rand((S, 1, 4), 42)
+    do = _rand((S, 2, 4), 43)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, threads=1, **kw)
+    h = 1e-6
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(arr)
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            ix = it.multi_index
+            a1, a2 = arr.copy(), arr.copy()
+            a1[ix] += h
+            a2[ix] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = a1
+            f1 = _loss(args["q"], args["k"], args["v"], do, **kw)
+            args[name] = a2
+            f2 = _loss(args["q"], args["k"], args["v"], do, **kw)
+            num[ix] = (f1 - f2) / (2 * h)
+        err = np.max(np.abs(num - grad)) / np.max(np.abs(grad))
+        assert err < 1e-6, (name, err)
+
+
+def test_backward_matches_torch_autograd():
+    lengths = [13, 4, 19]
+    S = sum(lengths)
+    pos = _packed_pos(lengths)
+    q, k, v = _rand((S, 4, 8), 44), _rand((S, 2, 8), 45), _rand((S, 2, 8), 46)
+    do = _rand((S, 4, 8), 47)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, pos=pos, causal=True)
+    mask = np.zeros((S, S), dtype=bool)
+    a = 0
+    for L in lengths:
+        mask[a:a + L, a:a + L] = np.tril(np.ones((L, L), dtype=bool))
+        a += L
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    rep = lambda t: t.permute(1, 0, 2).repeat_interleave(2, 0)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq.permute(1, 0, 2)[None], rep(tk), rep(tv), attn_mask=torch.from_numpy(mask))
+    o[0].permute(1, 0, 2).backward(torch.from_numpy(do))
+    for g, t in ((dq, tq), (dk, tk), (dv, tv)):
+        assert np.max(np.abs(g - t.grad.numpy())) < 1e-12
+
+
+def test_gradient_identities():
+    lengths = [25, 39]
+    S = sum(lengths)
+    pos = _packed_pos(lengths)
+    q, k, v = _rand((S, 4, 16), 48), _rand((S, 1, 16), 49), _rand((S, 1, 16), 50)
+    do = _rand((S, 4, 16), 51)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, pos=pos, causal=True)
+    # softmax rows sum to one => sum_j dS_ij = 0 => sum_j dK_j = 0 (per document)
+    a = 0
+    for L in lengths:
+        assert np.max(np.abs(dk[a:a + L].sum(axis=0))) < 1e-12
+        # sum_j dV_j = sum over the group's query heads of sum_i dO_i
+        assert np.max(np.abs(dv[a:a + L, 0].sum(axis=0) - do[a:a + L].sum(axis=(0, 1)))) < 1e-12
+        a += L
+
+
+def test_backward_sampled_rows_cover_late_keys():
+    S = 60
+    pos = np.arange(S, dtype=np.int32)
+    q, k, v = _rand((S, 2, 8), 52), _rand((S, 1, 8), 53), _rand((S, 1, 8), 54)
+    do = _rand((S, 2, 8), 55)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, pos=pos, causal=True)
+    rows = np.arange(45, 60)        # every row that can see keys 45..59
+    dq_s, dk_s, dv_s = oracle.attention_bwd(q, k, v, do, pos=pos, causal=True, rows=rows)
+    assert np.max(np.abs(dq_s - dq[rows])) < 1e-14
+    assert np.max(np.abs(dk_s[45:] - dk[45:])) < 1e-13
+    assert np.max(np.abs(dv_s[45:] - dv[45:])) < 1e-13
+
+
+# ---- permutes ----
+
+@pytest.mark.parametrize("P,S_l,H,D", [(2, 3, 4, 2), (4, 2, 8, 3), (3, 5, 3, 1), (1, 4, 2, 2)])
+def test_permute_brute_force_and_inverse(P, S_l, H, D):
+    x = np.arange(P * S_l * H * D, dtype=np.int64).reshape(P, S_l, H, D)
+    y = oracle.seq_to_head(x)
+    assert np.array_equal(y, oracle.seq_to_head_elementwise(x))
+    assert np.array_equal(oracle.head_to_seq(y), x)
+    # every element appears exactly once (bijection)
+    assert np.array_equal(np.sort(y.ravel()), np.arange(x.size))
+    out = np.full_like(x, -1)
+    for g in range(P):
+        yg = oracle.seq_to_head(x, group=g)
+        assert np.array_equal(yg, y[g])
+        oracle.head_to_seq(yg, out=out, group=g)
+    assert np.array_equal(out, x)
+
+
+def test_permute_adjoint_is_inverse():
+    x = _rand((4, 5, 8, 3), 56)
+    y = _rand((4, 20, 2, 3), 57)
+    lhs = np.sum(y * oracle.seq_to_head(x))
+    rhs = np.sum(oracle.head_to_seq(y) * x)
+    assert abs(lhs - rhs) < 1e-12
+
+
+def test_permute_token_order_matches_contiguous_sharding():
+    # rank s holds tokens [s*S_l, (s+1)*S_l): after the re-layout, rank g's share
+    # is the whole sequence in token order for its head subset
+    P, S_l, H, D = 4, 3, 8, 1
+    tok = np.arange(P * S_l)
+    x = np.zeros((P, S_l, H, D))
+    for s in range(P):
+        for h in range(H):
+            x[s, :, h, 0] = tok[s * S_l:(s + 1) * S_l] * 100 + h
+    for g in range(P):
+        yg = oracle.seq_to_head(x, group=g)
+        for hp in range(H // P):
+            assert np.array_equal(yg[:, hp, 0], tok * 100 + g * (H // P) + hp)
+
+
+# ---- input recipe facts ----
+
+def test_packed_doc_lengths_and_positions():
+    lengths = inputs.doc_lengths(131072, 16, 1)
+    assert lengths.sum() == 131072 and lengths.size == 16 and lengths.min() > 0
+    pos = inputs.position_ids(lengths)
+    starts = np.concatenate([[0], np.cumsum(lengths)[:-1]])
+    assert np.all(pos[starts] == 0)
+    assert pos.size == 131072 and pos.max() == lengths.max() - 1
