@@ -1,0 +1,291 @@
+"""Benchmark of the attention share on one MI355X.
+
+One step = one pass of the whole hot path over one batch: the Ulysses share of a
+sequence-parallel attention layer (8 ranks, 32 query heads, 8 key/value heads,
+head dim 128) at S = 131072 tokens in 16 packed documents, as rank 0 sees it:
+
+  1. sequence-shard -> head-shard re-layout of x_q, x_k, x_v ([8][16384][H][128]
+     -> q [131072][4][128], k, v [131072][1][128]);
+  2. blockattn_fwd (causal over packed documents via position_ids);
+  3. head-shard -> sequence-shard re-layout of O;
+  4. re-layout of the upstream gradient dO;
+  5. blockattn_bwd;
+  6. re-layout of dQ, dK, dV back to sequence shards.
+
+The share is exactly the packed long-context attention workload (4 query heads
+sharing 1 key/value head, 16 documents with multinomial lengths).  `value` is
+the whole step's throughput in causal-adjusted attention TFLOP/s (fwd 4*d*vis*Hq,
+bwd 2.5x that, vis = visible (query, key) pairs).  The merge of ring partials is
+not part of this step; it is timed on its own at the ring workload's shapes and
+reported under "components".
+
+Prints ONE JSON line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "causal attn fwd+bwd TFLOP/s & % bf16 MFMA peak at S=128k; permute GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+P, H_Q, H_KV, D = 8, 32, 8, 128
+S = 131072
+N_DOCS, DOC_SEED, SEED = 16, 1, 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the stand-alone permute and merge measurements")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import sequence_parallelism_amd as usp
+    from sequence_parallelism_amd import inputs
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    usp.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs, resident in HBM before timing -----------------------------------
+    lengths = inputs.doc_lengths(S, N_DOCS, DOC_SEED)
+    pos = torch.from_numpy(inputs.position_ids(lengths)).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(SEED)
+    S_l = S // P
+
+    def randn(*shape):
+        return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    xq, xk, xv = randn(P, S_l, H_Q, D), randn(P, S_l, H_KV, D), randn(P, S_l, H_KV, D)
+    xdo = randn(P, S_l, H_Q, D)
+    hq, hkv = H_Q // P, H_KV // P
+    q = torch.empty((S, hq, D), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((S, hkv, D), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    o = torch.empty_like(q)
+    lse = torch.empty((hq, S), dtype=torch.float32, device=dev)
+    do = torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    o_seq, dxq = torch.zeros_like(xq), torch.zeros_like(xq)
+    dxk, dxv = torch.zeros_like(xk), torch.zeros_like(xv)
+    ws = torch.empty(usp.bwd_workspace_bytes(S, hq, D), dtype=torch.uint8, device=dev)
+
+    vis = int(np.sum(lengths * (lengths + 1) // 2))
+    fwd_flop = 4.0 * D * vis * hq
+    bwd_flop = 2.5 * fwd_flop
+    eb = 2
+    perm_bytes = {  # algorithmic bytes: every element read once and written once
+        "seq_to_head_qkv": 2 * eb * (q.numel() + k.numel() + v.numel()),
+        "head_to_seq_o": 2 * eb * o.numel(),
+        "seq_to_head_do": 2 * eb * do.numel(),
+        "head_to_seq_grads": 2 * eb * (dq.numel() + dk.numel() + dv.numel()),
+    }
+    stream = torch.cuda.current_stream()
+    names = ["seq_to_head_qkv", "fwd", "head_to_seq_o", "seq_to_head_do", "bwd", "head_to_seq_grads"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        usp.seq_to_head(xq, P, group=0, out=q)
+        usp.seq_to_head(xk, P, group=0, out=k)
+        usp.seq_to_head(xv, P, group=0, out=v)
+        mark(1)
+        usp.blockattn_fwd(q, k, v, pos, o=o, lse=lse)
+        mark(2)
+        usp.head_to_seq(o, P, H_Q, out=o_seq, group=0)
+        mark(3)
+        usp.seq_to_head(xdo, P, group=0, out=do)
+        mark(4)
+        usp.blockattn_bwd(q, k, v, o, lse, do, pos, dq=dq, dk=dk, dv=dv, workspace=ws)
+        mark(5)
+        usp.head_to_seq(dq, P, H_Q, out=dxq, group=0)
+        usp.head_to_seq(dk, P, H_KV, out=dxk, group=0)
+        usp.head_to_seq(dv, P, H_KV, out=dxv, group=0)
+        mark(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-component HIP events on the launch stream, over the timed steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    comp_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+               for j, n in enumerate(names)}
+
+    step_s = ms_step / 1e3
+    value = (fwd_flop + bwd_flop) / step_s / 1e12
+    fwd_tf = fwd_flop / (comp_ms["fwd"] / 1e3) / 1e12
+    bwd_tf = bwd_flop / (comp_ms["bwd"] / 1e3) / 1e12
+    perm_ms = sum(comp_ms[n] for n in perm_bytes)
+    perm_gbps = sum(perm_bytes.values()) / (perm_ms / 1e3) / 1e9
+    components = {
+        "ms": {n: round(v_, 4) for n, v_ in comp_ms.items()},
+        "attn_fwd_TFLOPs": round(fwd_tf, 2),
+        "attn_bwd_TFLOPs": round(bwd_tf, 2),
+        "attn_fwd_frac_of_bf16_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+        "attn_bwd_frac_of_bf16_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+        "permute_GBps_in_step": round(perm_gbps, 1),
+        "permute_frac_of_hbm_peak_in_step": round(perm_gbps / PEAK_HBM_GBPS, 4),
+        "visible_pairs_per_head": vis,
+    }
+
+    # dominant launch: the backward call (its three kernels, timed together)
+    dominant = "bwd" if comp_ms["bwd"] >= comp_ms["fwd"] else "fwd"
+    dom_flop = bwd_flop if dominant == "bwd" else fwd_flop
+    achieved = dom_flop / (comp_ms[dominant] / 1e3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "blockattn_bwd (pre + main + post launches)" if dominant == "bwd"
+                else "blockattn_fwd"}
+
+    if not args.no_extras:
+        components.update(extra_measurements(torch, usp, dev, g))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(q, k, v, do, lengths, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Ulysses SP=8 share, packed long context: S=131072, 16 docs "
+                               "(multinomial lengths, seed 1), 4 query heads sharing 1 kv head, "
+                               "d=128, bf16; permutes + fwd + bwd",
+                   "S": S, "Hq": hq, "Hkv": hkv, "D": D, "sp": P, "layer_heads_q": H_Q,
+                   "layer_heads_kv": H_KV, "docs": N_DOCS},
+        "tokens_per_s": round(S / step_s, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "components": components,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def extra_measurements(torch, usp, dev, g):
+    """Stand-alone permute (full bijection of the Ulysses SP=8, 32-head layer) and
+    lse_merge (ring blocks of 16384 rows, 2 heads) bandwidth, buffers rotated so
+    that the working set exceeds the 256 MB last-level cache."""
+    res = {}
+    sets = 3
+    xs = [torch.randn((8, 4096, 32, 128), generator=g, device=dev).to(torch.bfloat16)
+          for _ in range(sets)]
+    ys = [torch.empty((8, 32768, 4, 128), dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+    for i in range(sets):
+        usp.seq_to_head(xs[i], 8, out=ys[i])
+    torch.cuda.synchronize()
+    n = 12
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        usp.seq_to_head(xs[i % sets], 8, out=ys[i % sets])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    nbytes = 2 * xs[0].numel() * 2
+    res["permute_full_sp8_GBps"] = round(nbytes / (ms / 1e3) / 1e9, 1)
+    res["permute_full_sp8_frac_of_hbm_peak"] = round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
+    e0.record()
+    for i in range(n):
+        usp.head_to_seq(ys[i % sets], 8, 32, out=xs[i % sets])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    res["permute_inverse_full_sp8_GBps"] = round(nbytes / (ms / 1e3) / 1e9, 1)
+    del xs, ys
+
+    blk, H, nb = 16384, 2, 16
+    acc = torch.zeros((nb * blk, H, 128), dtype=torch.float32, device=dev)
+    acc_l = torch.full((H, nb * blk), -float("inf"), dtype=torch.float32, device=dev)
+    parts = [torch.randn((blk, H, 128), generator=g, device=dev) for _ in range(2)]
+    pl = [torch.randn((H, blk), generator=g, device=dev) for _ in range(2)]
+    for i in range(nb):
+        usp.lse_merge(acc[i * blk:(i + 1) * blk], acc_l[:, i * blk:(i + 1) * blk], parts[0], pl[0])
+    torch.cuda.synchronize()
+    n = 4 * nb
+    e0.record()
+    for i in range(n):
+        b = i % nb
+        usp.lse_merge(acc[b * blk:(b + 1) * blk], acc_l[:, b * blk:(b + 1) * blk], parts[i % 2],
+                      pl[i % 2])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    nbytes = 3 * blk * H * 128 * 4 + 3 * H * blk * 4   # O_acc r/w + O_part r; LSE r/w + r
+    res["lse_merge_GBps"] = round(nbytes / (ms / 1e3) / 1e9, 1)
+    res["lse_merge_frac_of_hbm_peak"] = round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
+    res["lse_merge_us"] = round(ms * 1e3, 2)
+    return res
+
+
+def cpu_baseline(q, k, v, do, lengths, target_s):
+    """The fp64 CPU oracle, untuned, on a bounded sample of the same workload:
+    whole packed documents (fwd + bwd, all 4 query heads), taken in order until
+    about target_s seconds of CPU work."""
+    import oracle
+    import torch
+
+    threads = len(os.sched_getaffinity(0))
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    starts = np.concatenate([[0], np.cumsum(lengths)[:-1]])
+    done_flop, spent, docs = 0.0, 0.0, 0
+    hq = q.shape[1]
+    for a, L in zip(starts, lengths):
+        a, L = int(a), int(L)
+        sl = slice(a, a + L)
+        args = (f64(q[sl]), f64(k[sl]), f64(v[sl]))
+        dd = f64(do[sl])
+        pos = np.arange(L, dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.attention_fwd(*args, pos=pos, causal=True, threads=threads)
+        oracle.attention_bwd(*args, dd, pos=pos, causal=True, threads=threads)
+        spent += time.perf_counter() - t0
+        vis = L * (L + 1) // 2
+        done_flop += 3.5 * 4.0 * D * vis * hq
+        docs += 1
+        if spent >= target_s:
+            break
+    return {"value": round(done_flop / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{docs} whole document(s) of the packed S=131072 input "
+                      f"({int(sum(lengths[:docs]))} tokens, 4 query heads), fwd+bwd in fp64 numpy, "
+                      f"{spent:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

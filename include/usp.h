@@ -1,0 +1,184 @@
+/*
+ * usp.h -- C ABI of the MI355X (gfx950) attention share of a sequence-parallel layer.
+ *
+ * One GPU's part of a Ulysses / Ring sequence-parallel attention layer:
+ *   - the sequence-shard <-> head-shard re-layout that Ulysses' all-to-all performs,
+ *     done here as a local permutation on one GPU;
+ *   - exact blockwise softmax attention (forward and backward) over that share,
+ *     with the causal / packed-document mask given by O(n) position_ids;
+ *   - the merge of partial (O, LSE) results by the cumulative softmax.
+ *
+ * Conventions for every entry point
+ *   - Pointers named q, k, v, o, dout, dq, dk, dv, workspace, lse, position_ids,
+ *     src, dst, o_acc, o_part, lse_acc, lse_part are DEVICE pointers owned by the
+ *     caller.  A pointer to an empty tensor (a size of 0) may be NULL.  The
+ *     library allocates nothing, frees nothing, keeps no pointer after the call
+ *     returns and has no global mutable state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
+ *     work is enqueued on it in stream order; no call synchronises the device.
+ *   - Arguments are validated on the host before anything is enqueued: a call
+ *     that returns an error enqueues nothing.  No C++ exception crosses the ABI.
+ *   - Tensors are dense and row-major in the index order written ([a][b][c] means
+ *     c fastest).  bf16 is IEEE bfloat16 (round-to-nearest-even on output).
+ *   - Preconditions NOT checked on the device: position_ids well formed (0, 1, 2, ...
+ *     inside each packed document) and covering every global token index the call
+ *     touches; buffers large enough for the stated shapes; no overlap between
+ *     inputs and outputs unless stated.
+ */
+#ifndef USP_H
+#define USP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define USP_ABI_VERSION 1
+
+typedef enum {
+  USP_OK = 0,
+  USP_ERR_NULL_POINTER = 1,      /* a required pointer is NULL                       */
+  USP_ERR_BAD_SHAPE = 2,         /* a size is negative/zero where not allowed, or a
+                                    leading dimension is too small                  */
+  USP_ERR_NOT_DIVISIBLE = 3,     /* heads not divisible by ranks, or query heads not
+                                    a multiple of key/value heads                    */
+  USP_ERR_BAD_DTYPE = 4,         /* dtype value unknown or combination unsupported  */
+  USP_ERR_MISALIGNED = 5,        /* pointer not aligned as the entry point requires */
+  USP_ERR_WORKSPACE_TOO_SMALL = 6,
+  USP_ERR_UNSUPPORTED = 7,       /* valid but not implemented (e.g. head dim)       */
+  USP_ERR_HIP = 8                /* the HIP runtime reported a launch error          */
+} usp_status;
+
+typedef enum { USP_BF16 = 0, USP_F32 = 1 } usp_dtype;
+
+/* Version of this ABI (USP_ABI_VERSION). */
+int32_t usp_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* usp_status_string(usp_status status);
+
+/* ---------------------------------------------------------------------------
+ * Ulysses all-to-all #1 as a local permutation: sequence shards -> head shards.
+ *
+ * Defined by the Keryc article "Ulysses SP: entrenar modelos con millones de
+ * tokens", section "Como funciona Ulysses Sequence Parallelism (SP)", steps 1 and
+ * 3 (each GPU holds a contiguous chunk of tokens; the all-to-all gives each GPU
+ * every position for a subset of heads), and by the DeepSpeed-Ulysses notes,
+ * section "Method", all-to-all table ((N/P, d) -> (N, d/P)).
+ *
+ *   src  [P][S_local][H][D]  rank s holds tokens [s*S_local, (s+1)*S_local)
+ *   group < 0 :  dst [P][P*S_local][H/P][D]   every rank's share (a bijection)
+ *   group = g :  dst [P*S_local][H/P][D]      rank g's share only
+ *   dst[g][s*S_local + t][h'][:] = src[s][t][g*H/P + h'][:]
+ * Rank g receives the contiguous head block [g*H/P, (g+1)*H/P).
+ * dtype only sets the element size (bf16: 2 bytes, f32: 4 bytes); the copy is
+ * bitwise.  src and dst must not overlap.
+ * Errors: NULL pointers (when S_local > 0); P < 1, S_local < 0, H < 1, D < 1;
+ * H % P != 0; group >= P; unknown dtype.  S_local == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+usp_status usp_seq_to_head_permute(void* dst, const void* src, int32_t P, int64_t S_local,
+                                   int32_t H, int32_t D, usp_dtype dtype, int32_t group,
+                                   void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Ulysses all-to-all #2 as a local permutation: head shards -> sequence shards,
+ * the exact inverse of usp_seq_to_head_permute (Keryc article, same section,
+ * step 5; DeepSpeed-Ulysses notes, "Method", the second re-distribution of the
+ * attention output).
+ *
+ *   group < 0 :  src [P][P*S_local][H/P][D] -> dst [P][S_local][H][D]
+ *   group = g :  src [P*S_local][H/P][D] (rank g's share); only the head slice
+ *                [g*H/P, (g+1)*H/P) of dst [P][S_local][H][D] is written, the rest
+ *                of dst is left untouched.
+ * Errors as for usp_seq_to_head_permute.
+ * ------------------------------------------------------------------------- */
+usp_status usp_head_to_seq_permute(void* dst, const void* src, int32_t P, int64_t S_local,
+                                   int32_t H, int32_t D, usp_dtype dtype, int32_t group,
+                                   void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Exact blockwise attention forward over one share.
+ *
+ * Ultralytics glossary "Ring Attention", section "Como funciona la atencion en
+ * anillo": exact softmax attention computed block by block over key/value chunks
+ * with a running maximum, a running sum of exponentiated scores and a running
+ * weighted sum of values, divided at the end.  The causal / packed-document mask
+ * comes from O(n) position_ids (aitoolresearcher Ulysses SP review, section 3).
+ *
+ *   q [Sq][Hq][D], k [Sk][Hkv][D], v [Sk][Hkv][D]   (in_dtype)
+ *   Query row i is the global token q_start + i; key j is the global token k_start + j.
+ *   causal != 0: key gk is visible to query gq iff gq - pos[gq] <= gk <= gq, where
+ *                pos = position_ids (int32, indexed by global token).
+ *   causal == 0: every key is visible; position_ids may be NULL.
+ *   Query head h reads key/value head h / (Hq/Hkv).
+ *   o   [Sq][Hq][D] in o_dtype: softmax(scale * q k^T + mask) v.
+ *   lse [Hq][lse_ld] float32: natural-log sum of exp of the visible scaled scores
+ *       (row max + ln of the row sum).  A row with no visible key gets o = 0 and
+ *       lse = -inf.
+ * Supported: in_dtype BF16 with D = 128 (MFMA path; o_dtype BF16 or F32);
+ *            in_dtype F32 with 1 <= D <= 128 (o_dtype F32).
+ * Alignment: bf16 q, k, v, o 16-byte aligned.
+ * Errors: NULL pointers (position_ids only when causal); Sq, Sk < 0; Hq, Hkv < 1;
+ * Hq % Hkv; lse_ld < Sq; q_start, k_start < 0; unsupported dtype / D; misaligned.
+ * Sq == 0 or Sk == 0 is valid (Sk == 0 writes o = 0, lse = -inf).
+ * ------------------------------------------------------------------------- */
+usp_status blockattn_fwd(const void* q, const void* k, const void* v,
+                         int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D,
+                         const int32_t* position_ids, int64_t q_start, int64_t k_start,
+                         int32_t causal, float softmax_scale, usp_dtype in_dtype,
+                         void* o, usp_dtype o_dtype, float* lse, int64_t lse_ld,
+                         void* stream);
+
+/* Bytes of device workspace blockattn_bwd needs for these sizes. */
+usp_status blockattn_bwd_workspace_size(int64_t Sq, int32_t Hq, int32_t D, size_t* bytes);
+
+/* ---------------------------------------------------------------------------
+ * Backward of blockattn_fwd (the pages are silent on the backward pass; this is
+ * the analytic adjoint of the forward above).
+ *
+ *   inputs: q, k, v as for the forward; o [Sq][Hq][D] and lse [Hq][lse_ld] as the
+ *   forward wrote them (o in in_dtype); dout [Sq][Hq][D] (in_dtype).
+ *   outputs (in_dtype): dq [Sq][Hq][D], dk [Sk][Hkv][D], dv [Sk][Hkv][D]; dk and dv
+ *   of a key/value head are summed over the query heads that share it.
+ *     P = exp(scale q k^T + mask - lse), D_i = <dout_i, o_i>,
+ *     dv = P^T dout, dS = P * (dout v^T - D), dq = scale dS k, dk = scale dS^T q.
+ *   workspace: caller-owned device buffer of at least
+ *   blockattn_bwd_workspace_size() bytes, 256-byte aligned; its contents on entry
+ *   do not matter and are clobbered.
+ * Supported: in_dtype BF16 with D = 128.
+ * Errors: as for blockattn_fwd, plus USP_ERR_WORKSPACE_TOO_SMALL.
+ * ------------------------------------------------------------------------- */
+usp_status blockattn_bwd(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, int64_t lse_ld, const void* dout,
+                         int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D,
+                         const int32_t* position_ids, int64_t q_start, int64_t k_start,
+                         int32_t causal, float softmax_scale, usp_dtype in_dtype,
+                         void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * In-place merge of a partial attention result into an accumulator
+ * (Ring Attention glossary page, "Como funciona la atencion en anillo": partial
+ * results of the key blocks are combined by the same cumulative softmax).
+ *
+ *   (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_part, lse_part))
+ *     L = ln(e^{lse_acc} + e^{lse_part})
+ *     o = e^{lse_acc - L} o_acc + e^{lse_part - L} o_part
+ *   o_acc [S][H][D] (acc_dtype), lse_acc [H][lse_acc_ld] float32,
+ *   o_part [S][H][D] (part_dtype), lse_part [H][lse_part_ld] float32.
+ *   (o = 0, lse = -inf) is the identity: an accumulator initialised that way
+ *   becomes the first partial merged into it.
+ * Supported: acc_dtype F32 or BF16; part_dtype F32 or BF16; any D >= 1.
+ * Errors: NULL pointers; S < 0; H < 1; D < 1; leading dims < S; unknown dtype.
+ * ------------------------------------------------------------------------- */
+usp_status lse_merge(void* o_acc, usp_dtype acc_dtype, float* lse_acc, int64_t lse_acc_ld,
+                     const void* o_part, usp_dtype part_dtype, const float* lse_part,
+                     int64_t lse_part_ld, int64_t S, int32_t H, int32_t D, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* USP_H */

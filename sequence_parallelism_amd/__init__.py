@@ -1,0 +1,218 @@
+"""Python binding of libusp.so, the MI355X (gfx950) attention share of a
+sequence-parallel layer.
+
+Argument marshalling only: every call forwards device pointers, sizes and the
+current HIP stream to the C ABI declared in include/usp.h; all arithmetic runs in
+the library's HIP kernels.  PyTorch provides device memory and streams.  There
+is no fallback: if the built library is missing, every entry point raises.
+"""
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libusp.so")
+
+BF16, F32 = 0, 1
+
+STATUS = {
+    0: "USP_OK", 1: "USP_ERR_NULL_POINTER", 2: "USP_ERR_BAD_SHAPE", 3: "USP_ERR_NOT_DIVISIBLE",
+    4: "USP_ERR_BAD_DTYPE", 5: "USP_ERR_MISALIGNED", 6: "USP_ERR_WORKSPACE_TOO_SMALL",
+    7: "USP_ERR_UNSUPPORTED", 8: "USP_ERR_HIP",
+}
+
+# name -> (restype, argtypes) exactly as declared in include/usp.h
+_c_int32, _c_int64, _c_float, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+SIGNATURES = {
+    "usp_abi_version": (_c_int32, []),
+    "usp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "usp_seq_to_head_permute": (ctypes.c_int, [_vp, _vp, _c_int32, _c_int64, _c_int32, _c_int32,
+                                               ctypes.c_int, _c_int32, _vp]),
+    "usp_head_to_seq_permute": (ctypes.c_int, [_vp, _vp, _c_int32, _c_int64, _c_int32, _c_int32,
+                                               ctypes.c_int, _c_int32, _vp]),
+    "blockattn_fwd": (ctypes.c_int, [_vp, _vp, _vp, _c_int64, _c_int64, _c_int32, _c_int32,
+                                     _c_int32, _vp, _c_int64, _c_int64, _c_int32, _c_float,
+                                     ctypes.c_int, _vp, ctypes.c_int, _vp, _c_int64, _vp]),
+    "blockattn_bwd_workspace_size": (ctypes.c_int, [_c_int64, _c_int32, _c_int32,
+                                                    ctypes.POINTER(ctypes.c_size_t)]),
+    "blockattn_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_int64, _vp, _c_int64, _c_int64,
+                                     _c_int32, _c_int32, _c_int32, _vp, _c_int64, _c_int64,
+                                     _c_int32, _c_float, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _vp]),
+    "lse_merge": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _c_int64, _vp, ctypes.c_int, _vp,
+                                 _c_int64, _c_int64, _c_int32, _c_int32, _vp]),
+}
+
+_lib = None
+
+
+class UspError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        msg = _lib.usp_status_string(status).decode() if _lib is not None else ""
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({msg})")
+
+
+def load():
+    """Load libusp.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                           "(run python -m sequence_parallelism_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise UspError(fn, status)
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t, name):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+# ---- Ulysses re-layout ----------------------------------------------------------
+
+def seq_to_head(src, P, group=-1, out=None, stream=None):
+    """[P][S_l][H][D] -> [P][P*S_l][H/P][D] (group < 0) or [P*S_l][H/P][D] (group g)."""
+    import torch
+    lib = load()
+    _need(src, "src")
+    P_, S_l, H, D = src.shape
+    if P_ != P:
+        raise ValueError("src leading dim must equal P")
+    shape = (P, P * S_l, H // P, D) if group < 0 else (P * S_l, H // P, D)
+    if out is None:
+        out = torch.empty(shape, dtype=src.dtype, device=src.device)
+    _need(out, "out")
+    _check("usp_seq_to_head_permute",
+           lib.usp_seq_to_head_permute(_ptr(out), _ptr(src), P, S_l, H, D, _dtype_code(src),
+                                       group, _stream(stream)))
+    return out
+
+
+def head_to_seq(src, P, H, out=None, group=-1, stream=None):
+    """Inverse of seq_to_head.  group g writes only heads [g*H/P, (g+1)*H/P) of out."""
+    import torch
+    lib = load()
+    _need(src, "src")
+    if group < 0:
+        _, S, Hp, D = src.shape
+    else:
+        S, Hp, D = src.shape
+    S_l = S // P
+    if out is None:
+        if group >= 0:
+            raise ValueError("group form writes into an existing [P][S_l][H][D] tensor")
+        out = torch.empty((P, S_l, H, D), dtype=src.dtype, device=src.device)
+    _need(out, "out")
+    _check("usp_head_to_seq_permute",
+           lib.usp_head_to_seq_permute(_ptr(out), _ptr(src), P, S_l, H, D, _dtype_code(src),
+                                       group, _stream(stream)))
+    return out
+
+
+# ---- attention --------------------------------------------------------------------
+
+def blockattn_fwd(q, k, v, position_ids=None, q_start=0, k_start=0, causal=True, scale=None,
+                  o=None, lse=None, o_dtype=None, stream=None):
+    """q [Sq][Hq][D], k, v [Sk][Hkv][D] -> (o [Sq][Hq][D], lse [Hq][Sq] float32)."""
+    import torch
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n)
+    Sq, Hq, D = q.shape
+    Sk, Hkv, _ = k.shape
+    scale = D ** -0.5 if scale is None else float(scale)
+    if o is None:
+        o = torch.empty((Sq, Hq, D), dtype=o_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((Hq, Sq), dtype=torch.float32, device=q.device)
+    _need(o, "o")
+    if position_ids is not None:
+        _need(position_ids, "position_ids")
+        if position_ids.dtype != torch.int32:
+            raise TypeError("position_ids must be int32")
+    _check("blockattn_fwd",
+           lib.blockattn_fwd(_ptr(q), _ptr(k), _ptr(v), Sq, Sk, Hq, Hkv, D, _ptr(position_ids),
+                             q_start, k_start, int(bool(causal)), scale, _dtype_code(q),
+                             _ptr(o), _dtype_code(o), _ptr(lse), lse.stride(0), _stream(stream)))
+    return o, lse
+
+
+def bwd_workspace_bytes(Sq, Hq, D):
+    lib = load()
+    n = ctypes.c_size_t(0)
+    _check("blockattn_bwd_workspace_size",
+           lib.blockattn_bwd_workspace_size(Sq, Hq, D, ctypes.byref(n)))
+    return n.value
+
+
+def blockattn_bwd(q, k, v, o, lse, dout, position_ids=None, q_start=0, k_start=0, causal=True,
+                  scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of blockattn_fwd for upstream gradient dout."""
+    import torch
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n)
+    Sq, Hq, D = q.shape
+    Sk, Hkv, _ = k.shape
+    scale = D ** -0.5 if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = bwd_workspace_bytes(Sq, Hq, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check("blockattn_bwd",
+           lib.blockattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), lse.stride(0),
+                             _ptr(dout), Sq, Sk, Hq, Hkv, D, _ptr(position_ids), q_start, k_start,
+                             int(bool(causal)), scale, _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(stream)))
+    return dq, dk, dv
+
+
+def lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
+    """In place: (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_part, lse_part))."""
+    lib = load()
+    for t, n in ((o_acc, "o_acc"), (o_part, "o_part")):
+        _need(t, n)
+    S, H, D = o_acc.shape
+    _check("lse_merge",
+           lib.lse_merge(_ptr(o_acc), _dtype_code(o_acc), _ptr(lse_acc), lse_acc.stride(0),
+                         _ptr(o_part), _dtype_code(o_part), _ptr(lse_part), lse_part.stride(0),
+                         S, H, D, _stream(stream)))
+    return o_acc, lse_acc
+
+
+__all__ = ["load", "seq_to_head", "head_to_seq", "blockattn_fwd", "blockattn_bwd",
+           "bwd_workspace_bytes", "lse_merge", "UspError", "BF16", "F32", "SIGNATURES"]

@@ -1,0 +1,73 @@
+// Internal helpers shared by the HIP kernels and the ABI layer (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/usp.h"
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define USP_LOG2E 1.4426950408889634f
+#define USP_LN2 0.6931471805599453f
+
+// Launchers (host functions) implemented next to their kernels.  They assume the
+// arguments were validated by the ABI layer and return the launch status.
+struct PermuteArgs {
+  void* dst;
+  const void* src;
+  int32_t P;
+  int64_t S_local;
+  int32_t H;
+  int32_t D;
+  int32_t esize;      // element size in bytes
+  int32_t group;      // <0: all ranks
+  int32_t to_head;    // 1: seq->head, 0: head->seq
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* pos;
+  void* o;
+  float* lse;
+  int64_t lse_ld;
+  int32_t Sq, Sk, Hq, Hkv, D;
+  int32_t q_start, k_start;
+  int32_t causal;
+  float scale;
+};
+hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t s);
+hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t s);
+
+struct AttnBwdArgs {
+  AttnArgs f;          // q, k, v, pos, o (forward output), lse, sizes
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;        // workspace: [Hq][Sq]
+  float* dq_acc;       // workspace: [Sq][Hq][D] fp32
+};
+size_t attn_bwd_workspace_bytes(int64_t Sq, int32_t Hq, int32_t D);
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s);
+
+struct MergeArgs {
+  void* o_acc;
+  float* lse_acc;
+  int64_t lse_acc_ld;
+  const void* o_part;
+  const float* lse_part;
+  int64_t lse_part_ld;
+  int64_t S;
+  int32_t H, D;
+  int32_t acc_f32, part_f32;
+};
+hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);

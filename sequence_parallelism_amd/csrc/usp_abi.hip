@@ -1,0 +1,179 @@
+// C ABI of the attention share: host-side argument validation and dispatch.
+// Every check runs before anything is enqueued, so a failing call has no effect.
+#include <climits>
+
+#include "common.h"
+
+namespace {
+
+constexpr int64_t I32_MAX = INT_MAX;
+
+bool bad_dtype(usp_dtype d) { return d != USP_BF16 && d != USP_F32; }
+int esize(usp_dtype d) { return d == USP_F32 ? 4 : 2; }
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+usp_status hip_status(hipError_t e) { return e == hipSuccess ? USP_OK : USP_ERR_HIP; }
+
+usp_status check_permute(const void* dst, const void* src, int32_t P, int64_t S_local, int32_t H,
+                         int32_t D, usp_dtype dtype, int32_t group) {
+  if (bad_dtype(dtype)) return USP_ERR_BAD_DTYPE;
+  if (P < 1 || S_local < 0 || H < 1 || D < 1) return USP_ERR_BAD_SHAPE;
+  if ((!dst || !src) && S_local > 0) return USP_ERR_NULL_POINTER;   // empty tensors may be NULL
+  if (H % P) return USP_ERR_NOT_DIVISIBLE;
+  if (group >= P) return USP_ERR_BAD_SHAPE;
+  // per (rank, rank) block: S_local runs of (H/P)*D elements, indexed in 32 bits
+  const int64_t block_bytes = S_local * (int64_t)(H / P) * D * esize(dtype);
+  if (block_bytes / 2 >= (int64_t)UINT_MAX) return USP_ERR_UNSUPPORTED;
+  if ((int64_t)P * P > 65535) return USP_ERR_UNSUPPORTED;
+  return USP_OK;
+}
+
+usp_status check_attn(const void* q, const void* k, const void* v, int64_t Sq, int64_t Sk,
+                      int32_t Hq, int32_t Hkv, int32_t D, const int32_t* pos, int64_t q_start,
+                      int64_t k_start, int32_t causal, usp_dtype in_dt, const void* o,
+                      const float* lse, int64_t lse_ld) {
+  // a pointer to an empty tensor may be NULL
+  if (Sq > 0 && (!q || !o || !lse)) return USP_ERR_NULL_POINTER;
+  if (Sk > 0 && (!k || !v)) return USP_ERR_NULL_POINTER;
+  if (causal && !pos && Sq > 0 && Sk > 0) return USP_ERR_NULL_POINTER;
+  if (bad_dtype(in_dt)) return USP_ERR_BAD_DTYPE;
+  if (Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1 || q_start < 0 || k_start < 0)
+    return USP_ERR_BAD_SHAPE;
+  if (lse_ld < Sq) return USP_ERR_BAD_SHAPE;
+  if (Hq % Hkv) return USP_ERR_NOT_DIVISIBLE;
+  // global token indices and element offsets are 32/64-bit in the kernels
+  if (q_start + Sq > I32_MAX || k_start + Sk > I32_MAX) return USP_ERR_UNSUPPORTED;
+  if (Sq * Hq > I32_MAX || Sk * Hkv > I32_MAX) return USP_ERR_UNSUPPORTED;
+  if (in_dt == USP_BF16 && D != 128) return USP_ERR_UNSUPPORTED;
+  if (in_dt == USP_F32 && D > 128) return USP_ERR_UNSUPPORTED;
+  if (in_dt == USP_BF16 && !(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(o, 16)))
+    return USP_ERR_MISALIGNED;
+  if (in_dt == USP_F32 && !(aligned(q, 4) && aligned(k, 4) && aligned(v, 4) && aligned(o, 4)))
+    return USP_ERR_MISALIGNED;
+  if (!aligned(lse, 4) || (pos && !aligned(pos, 4))) return USP_ERR_MISALIGNED;
+  return USP_OK;
+}
+
+AttnArgs make_args(const void* q, const void* k, const void* v, int64_t Sq, int64_t Sk, int32_t Hq,
+                   int32_t Hkv, int32_t D, const int32_t* pos, int64_t q_start, int64_t k_start,
+                   int32_t causal, float scale, void* o, float* lse, int64_t lse_ld) {
+  AttnArgs a;
+  a.q = q; a.k = k; a.v = v; a.pos = pos; a.o = o; a.lse = lse; a.lse_ld = lse_ld;
+  a.Sq = (int32_t)Sq; a.Sk = (int32_t)Sk; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
+  a.q_start = (int32_t)q_start; a.k_start = (int32_t)k_start;
+  a.causal = causal ? 1 : 0;
+  a.scale = scale;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t usp_abi_version(void) { return USP_ABI_VERSION; }
+
+const char* usp_status_string(usp_status st) {
+  switch (st) {
+    case USP_OK: return "ok";
+    case USP_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case USP_ERR_BAD_SHAPE: return "bad shape, size or leading dimension";
+    case USP_ERR_NOT_DIVISIBLE: return "heads not divisible (H % P or Hq % Hkv)";
+    case USP_ERR_BAD_DTYPE: return "unknown or unsupported dtype";
+    case USP_ERR_MISALIGNED: return "pointer not aligned as required";
+    case USP_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case USP_ERR_UNSUPPORTED: return "unsupported configuration";
+    case USP_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+usp_status usp_seq_to_head_permute(void* dst, const void* src, int32_t P, int64_t S_local, int32_t H,
+                                   int32_t D, usp_dtype dtype, int32_t group, void* stream) {
+  usp_status st = check_permute(dst, src, P, S_local, H, D, dtype, group);
+  if (st != USP_OK) return st;
+  PermuteArgs a{dst, src, P, S_local, H, D, esize(dtype), group < 0 ? -1 : group, 1};
+  return hip_status(launch_permute(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+usp_status usp_head_to_seq_permute(void* dst, const void* src, int32_t P, int64_t S_local, int32_t H,
+                                   int32_t D, usp_dtype dtype, int32_t group, void* stream) {
+  usp_status st = check_permute(dst, src, P, S_local, H, D, dtype, group);
+  if (st != USP_OK) return st;
+  PermuteArgs a{dst, src, P, S_local, H, D, esize(dtype), group < 0 ? -1 : group, 0};
+  return hip_status(launch_permute(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+usp_status blockattn_fwd(const void* q, const void* k, const void* v, int64_t Sq, int64_t Sk,
+                         int32_t Hq, int32_t Hkv, int32_t D, const int32_t* position_ids,
+                         int64_t q_start, int64_t k_start, int32_t causal, float softmax_scale,
+                         usp_dtype in_dtype, void* o, usp_dtype o_dtype, float* lse, int64_t lse_ld,
+                         void* stream) {
+  usp_status st = check_attn(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal,
+                             in_dtype, o, lse, lse_ld);
+  if (st != USP_OK) return st;
+  if (bad_dtype(o_dtype) || (in_dtype == USP_F32 && o_dtype != USP_F32)) return USP_ERR_BAD_DTYPE;
+  if (o_dtype == USP_F32 && !aligned(o, 16) && in_dtype == USP_BF16) return USP_ERR_MISALIGNED;
+  AttnArgs a = make_args(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal,
+                         softmax_scale, o, lse, lse_ld);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (in_dtype == USP_BF16) return hip_status(launch_attn_fwd_bf16(a, o_dtype == USP_F32, s));
+  return hip_status(launch_attn_fwd_f32(a, s));
+}
+
+usp_status blockattn_bwd_workspace_size(int64_t Sq, int32_t Hq, int32_t D, size_t* bytes) {
+  if (!bytes) return USP_ERR_NULL_POINTER;
+  if (Sq < 0 || Hq < 1 || D < 1) return USP_ERR_BAD_SHAPE;
+  *bytes = attn_bwd_workspace_bytes(Sq, Hq, D);
+  return USP_OK;
+}
+
+usp_status blockattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         int64_t lse_ld, const void* dout, int64_t Sq, int64_t Sk, int32_t Hq,
+                         int32_t Hkv, int32_t D, const int32_t* position_ids, int64_t q_start,
+                         int64_t k_start, int32_t causal, float softmax_scale, usp_dtype in_dtype,
+                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  usp_status st = check_attn(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal,
+                             in_dtype, o, lse, lse_ld);
+  if (st != USP_OK) return st;
+  if (Sq > 0 && (!dout || !dq)) return USP_ERR_NULL_POINTER;
+  if (Sk > 0 && (!dk || !dv)) return USP_ERR_NULL_POINTER;
+  if (!workspace && attn_bwd_workspace_bytes(Sq, Hq, D) > 0) return USP_ERR_NULL_POINTER;
+  if (in_dtype != USP_BF16) return USP_ERR_UNSUPPORTED;
+  if (!(aligned(dout, 16) && aligned(dq, 16) && aligned(dk, 8) && aligned(dv, 8) &&
+        aligned(workspace, 256)))
+    return USP_ERR_MISALIGNED;
+  const size_t need = attn_bwd_workspace_bytes(Sq, Hq, D);
+  if (workspace_bytes < need) return USP_ERR_WORKSPACE_TOO_SMALL;
+  AttnBwdArgs a;
+  a.f = make_args(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal, softmax_scale,
+                  const_cast<void*>(o), const_cast<float*>(lse), lse_ld);
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = reinterpret_cast<float*>(workspace);
+  a.dq_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                      (((size_t)Sq * Hq * sizeof(float) + 255) & ~(size_t)255));
+  return hip_status(launch_attn_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+usp_status lse_merge(void* o_acc, usp_dtype acc_dtype, float* lse_acc, int64_t lse_acc_ld,
+                     const void* o_part, usp_dtype part_dtype, const float* lse_part,
+                     int64_t lse_part_ld, int64_t S, int32_t H, int32_t D, void* stream) {
+  if (bad_dtype(acc_dtype) || bad_dtype(part_dtype)) return USP_ERR_BAD_DTYPE;
+  if (S < 0 || H < 1 || D < 1 || lse_acc_ld < S || lse_part_ld < S) return USP_ERR_BAD_SHAPE;
+  if (S > 0 && (!o_acc || !lse_acc || !o_part || !lse_part)) return USP_ERR_NULL_POINTER;
+  if (!aligned(o_acc, esize(acc_dtype)) || !aligned(o_part, esize(part_dtype)) ||
+      !aligned(lse_acc, 4) || !aligned(lse_part, 4))
+    return USP_ERR_MISALIGNED;
+  if (S * H > I32_MAX * 64LL) return USP_ERR_UNSUPPORTED;
+  MergeArgs a;
+  a.o_acc = o_acc; a.lse_acc = lse_acc; a.lse_acc_ld = lse_acc_ld;
+  a.o_part = o_part; a.lse_part = lse_part; a.lse_part_ld = lse_part_ld;
+  a.S = S; a.H = H; a.D = D;
+  a.acc_f32 = acc_dtype == USP_F32; a.part_f32 = part_dtype == USP_F32;
+  return hip_status(launch_lse_merge(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
