@@ -7,32 +7,60 @@
 //
 // Three kernels:
 //   1. pre:  D_i for every (row, head) and zeroing of the fp32 dQ accumulator;
-//   2. main: a workgroup owns 128 keys of one key/value head (32 per wave, kept
-//            as MFMA B-operand fragments in registers) and walks the query tiles
-//            that can see them, 32 rows at a time, for every query head of the
-//            group.  Per tile it recomputes S = Q K^T and dP = dO V^T with
-//            v_mfma_f32_32x32x16_bf16 (one key per lane, 16 query rows in
-//            registers), forms P and dS in registers, accumulates
-//            dV^T += dO^T P and dK^T += Q^T dS in registers, and adds
-//            dQ = dS K for the tile into the fp32 accumulator with coalesced
-//            atomics (dS goes through LDS once to change lane ownership);
+//   2. main: a workgroup owns 128 keys of one key/value head (32 per wave; K and V
+//            of those keys are MFMA B-operand fragments in registers, and the
+//            block's K is also staged row-major in LDS for dQ) and walks the
+//            query tiles that can see them, 64 rows at a time, for every query
+//            head of the group.  Query / dO tiles are double-buffered in LDS and
+//            the next one is fetched into registers while the current one is
+//            computed.  Per tile each wave recomputes S = Q K^T and dP = dO V^T
+//            with v_mfma_f32_32x32x16_bf16 (one key per lane, query rows in
+//            registers), forms P and dS in registers, and accumulates
+//            dV^T += dO^T P and dK^T += Q^T dS in registers, reading the
+//            transposed operands with the gfx950 transposing LDS read.  dS^T goes
+//            to LDS once; each wave then forms dQ for 32 of the 128 head-dim
+//            columns over the block's 128 keys and adds it to the fp32
+//            accumulator with atomics that are coalesced along the head dim;
 //   3. post: dQ accumulator -> bf16.
-// Query tiles that cannot see the key block are not visited; fully visible
-// (tile, block) pairs skip the per-element mask.
+// Query tiles that cannot see the key block are not visited (the first visible
+// tile follows from the block's first key, the last from a binary search over
+// document starts); waves whose keys a tile cannot see skip its matrix work, and
+// fully visible (tile, wave) pairs skip the per-element mask.
 #include "common.h"
 
 namespace {
 
 constexpr int HD = 128;
-constexpr int BKV = 128;            // keys per workgroup (4 waves x 32)
-constexpr int BQ = 32;              // query rows per inner step
-constexpr int QS_LD = HD + 8;       // row-major Q / dO tile pitch (bf16 elements)
-constexpr int QT_LD = BQ + 8;       // transposed Q / dO tile pitch
-constexpr int KT_LD = BKV + 8;      // transposed K block pitch
-constexpr int DS_LD = BKV + 8;      // dS tile pitch
+constexpr int NWB = 4;              // wavefronts per workgroup
+constexpr int BKV = 32 * NWB;       // keys per workgroup
+constexpr int BQ = 64;              // query rows per step
+constexpr int QS_LD = HD + 8;       // Q / dO tile pitch (bf16): 272 B
+constexpr int KS_LD = HD + 16;      // K block pitch (bf16): 288 B (transposing reads)
+constexpr int DS_LD = BQ + 8;       // dS^T tile pitch (bf16): 144 B
+static_assert(BKV * HD / 8 == 8 * NWB * 64, "K block staging moves eight 16-byte chunks per thread");
+static_assert((BQ * HD / 8) % (NWB * 64) == 0, "query tile staging splits evenly over threads");
+static_assert(BQ <= NWB * 64, "one thread per query row stages the row scalars");
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read: within each 16-lane group, source lane s points at
+// M[k0 + s/4][m0 + 4*(s%4) .. +3] of a row-major tile; lane i receives
+// M[k0 .. k0+3][m0 + i].
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+// MFMA operand of 8 consecutive reduction indices (k-slots k0 + 8(j/4) + 4*hi + j%4)
+// for lane column m, from a row-major [k][m] tile at p = &M[k0 + rowoff][m0 + coloff].
+__device__ __forceinline__ bf16x8 tr_operand(const bf16* p, int pitch) {
+  const bf16x4 a = lds_read_tr(p);
+  const bf16x4 b = lds_read_tr(p + 8 * pitch);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 __device__ __forceinline__ int wave_min(int x) {
@@ -69,28 +97,36 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
 }
 
 // ---- 2. main ----------------------------------------------------------------------
-__global__ __launch_bounds__(256) void attn_bwd_main_kernel(AttnBwdArgs a, int n_qtiles) {
-  __shared__ __attribute__((aligned(16))) bf16 Qs[BQ * QS_LD];
-  __shared__ __attribute__((aligned(16))) bf16 Qt[HD * QT_LD];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[BQ * QS_LD];
-  __shared__ __attribute__((aligned(16))) bf16 dOt[HD * QT_LD];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[HD * KT_LD];
-  __shared__ __attribute__((aligned(16))) bf16 dSs[BQ * DS_LD];
-  __shared__ float lse2_s[BQ], delta_s[BQ];
-  __shared__ int dsq_s[BQ], gq_s[BQ];
+__global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, int n_qtiles) {
+  __shared__ __attribute__((aligned(16))) bf16 Qs[2][BQ * QS_LD];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[2][BQ * QS_LD];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BKV * KS_LD];
+  __shared__ __attribute__((aligned(16))) bf16 dSt[BKV * DS_LD];
+  __shared__ __attribute__((aligned(16))) float lse2_s[2][BQ];
+  __shared__ __attribute__((aligned(16))) float delta_s[2][BQ];
+  __shared__ __attribute__((aligned(16))) int dsq_s[2][BQ];
+  __shared__ __attribute__((aligned(16))) int gq_s[2][BQ];
 
   const AttnArgs& f = a.f;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r32 = lane & 31, hi = lane >> 5;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int tr_row = 4 * hi + (i16 >> 2);              // transposing-read lane offsets
+  const int tr_col = 16 * (g16 & 1) + 4 * (i16 & 3);
   const int hk = blockIdx.x % f.Hkv;
-  const int k0 = (int)(blockIdx.x / f.Hkv) * BKV;   // local first key of the block
-  const int kl = k0 + wave * 32 + r32;                 // this lane's key (B-operand column)
+  const int k0 = (int)(blockIdx.x / f.Hkv) * BKV;      // local first key of the block
+  const int kw0 = k0 + wave * 32;                       // this wave's first key
+  const int kl = kw0 + r32;                             // this lane's key (B-operand column)
   const bool key_ok = kl < f.Sk;
   const int gk = f.k_start + kl;
   const int gk_first = f.k_start + k0;
   const int gk_last = f.k_start + min(k0 + BKV, f.Sk) - 1;
-  const bool keys_full = k0 + BKV <= f.Sk;
+  const int gkw_first = f.k_start + kw0;
+  const int gkw_last = f.k_start + min(kw0 + 32, f.Sk) - 1;
+  const bool wave_has_keys = kw0 < f.Sk;
+  const bool wave_keys_full = kw0 + 32 <= f.Sk;
   const int grp = f.Hq / f.Hkv;
+  const float sl2 = f.scale * USP_LOG2E;
 
   const bf16* __restrict__ qp = reinterpret_cast<const bf16*>(f.q);
   const bf16* __restrict__ kp = reinterpret_cast<const bf16*>(f.k);
@@ -108,126 +144,204 @@ __global__ __launch_bounds__(256) void attn_bwd_main_kernel(AttnBwdArgs a, int n
       vf[kk] = key_ok ? *reinterpret_cast<const bf16x8*>(vp + off + 16 * kk) : z;
     }
   }
-  // K^T of the whole key block in LDS (B operand of dQ = dS K)
+  // the block's K, row-major in LDS (B operand of dQ = dS K via transposing reads)
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
-    const int c = tid + 256 * it;
+    const int c = tid + NWB * 64 * it;
     const int key = c >> 4, dc = c & 15;
     bf16x8 kv = {};
-    if (k0 + key < f.Sk) kv = *reinterpret_cast<const bf16x8*>(kp + ((int64_t)(k0 + key) * f.Hkv + hk) * HD + dc * 8);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) Kt[(dc * 8 + j) * KT_LD + key] = kv[j];
+    if (k0 + key < f.Sk)
+      kv = *reinterpret_cast<const bf16x8*>(kp + ((int64_t)(k0 + key) * f.Hkv + hk) * HD + dc * 8);
+    *reinterpret_cast<bf16x8*>(&Ks[key * KS_LD + dc * 8]) = kv;
   }
+
+  // ---- query tiles that can see the block: [t0, t1) ------------------------------
+  int t0 = 0, t1 = n_qtiles;
+  if (f.causal) {
+    t0 = min(max(gk_first - f.q_start, 0) / BQ, n_qtiles);
+    // first tile whose first row starts its document after the block's last key
+    int lo_t = t0, hi_t = n_qtiles;
+    while (lo_t < hi_t) {
+      const int mid = (lo_t + hi_t) >> 1;
+      const int g = f.q_start + mid * BQ;
+      if (g - f.pos[g] > gk_last) hi_t = mid; else lo_t = mid + 1;
+    }
+    t1 = lo_t;
+  }
+  const int ntile = t1 - t0;
+  const int n_items = ntile * grp;
+
+  // ---- staging of one (head, tile) item: 64 rows of Q and dO + per-row scalars ----
+  constexpr int CHUNKS = BQ * HD / 8 / (NWB * 64);   // 16-byte chunks per thread per tile
+  bf16x8 pq[CHUNKS], pd[CHUNKS];
+  float p_lse = 0.f, p_delta = 0.f;
+  int p_ds = 0, p_gq = 0;
+  auto load_item = [&](int it) {
+    const int h = hk * grp + it / ntile;
+    const int q0 = (t0 + it % ntile) * BQ;
+#pragma unroll
+    for (int u = 0; u < CHUNKS; ++u) {
+      const int c = tid + NWB * 64 * u;
+      const int r = q0 + (c >> 4);
+      bf16x8 z = {};
+      pq[u] = z;
+      pd[u] = z;
+      if (r < f.Sq) {
+        const int64_t off = ((int64_t)r * f.Hq + h) * HD + (c & 15) * 8;
+        pq[u] = *reinterpret_cast<const bf16x8*>(qp + off);
+        pd[u] = *reinterpret_cast<const bf16x8*>(dop + off);
+      }
+    }
+    if (tid < BQ) {
+      const int r = q0 + tid;
+      const bool ok = r < f.Sq;
+      const int g = f.q_start + r;
+      p_lse = ok ? f.lse[(int64_t)h * f.lse_ld + r] * USP_LOG2E : 0.f;
+      p_delta = ok ? a.delta[(int64_t)h * f.Sq + r] : 0.f;
+      p_ds = !ok ? 0x7fffffff : (f.causal ? g - f.pos[g] : -0x7fffffff);
+      p_gq = !ok ? -0x7fffffff : (f.causal ? g : 0x7fffffff);
+    }
+  };
+  auto store_item = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CHUNKS; ++u) {
+      const int c = tid + NWB * 64 * u;
+      *reinterpret_cast<bf16x8*>(&Qs[buf][(c >> 4) * QS_LD + (c & 15) * 8]) = pq[u];
+      *reinterpret_cast<bf16x8*>(&dOs[buf][(c >> 4) * QS_LD + (c & 15) * 8]) = pd[u];
+    }
+    if (tid < BQ) {
+      lse2_s[buf][tid] = p_lse;
+      delta_s[buf][tid] = p_delta;
+      dsq_s[buf][tid] = p_ds;
+      gq_s[buf][tid] = p_gq;
+    }
+  };
 
   f32x16 dka[4], dva[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) { dka[i] = f32x16{}; dva[i] = f32x16{}; }
 
-  const float sl2 = f.scale * USP_LOG2E;
-  const int t0 = f.causal ? max(gk_first - f.q_start, 0) / BQ : 0;
+  if (n_items > 0) {
+    load_item(0);
+    store_item(0);
+    if (n_items > 1) load_item(1);
+  }
+  for (int it = 0; it < n_items; ++it) {
+    const int buf = it & 1;
+    const int h = hk * grp + it / ntile;
+    const int q0 = (t0 + it % ntile) * BQ;
+    __syncthreads();   // item `it` staged; dSt free
+    const bf16* Qb = Qs[buf];
+    const bf16* Db = dOs[buf];
 
-  for (int h = hk * grp; h < (hk + 1) * grp; ++h) {
-    for (int qt = t0; qt < n_qtiles; ++qt) {
-      const int q0 = qt * BQ;
-      if (f.causal) {
-        const int gq_a = f.q_start + q0;
-        if (gq_a - f.pos[gq_a] > gk_last) break;   // later tiles start later documents
-      }
-      __syncthreads();   // previous tile's LDS reads are done
-      // ---- stage Q, dO (row-major and transposed), lse, D, mask bounds ----------
+    // visibility of this wave's keys for the tile (wave-uniform)
+    const int t_dsmax = __builtin_amdgcn_readfirstlane(wave_max(dsq_s[buf][lane]));
+    const int t_dsmin = __builtin_amdgcn_readfirstlane(wave_min(dsq_s[buf][lane]));
+    const int t_gqmin = __builtin_amdgcn_readfirstlane(wave_min(gq_s[buf][lane]));
+    const int t_gqmax = __builtin_amdgcn_readfirstlane(wave_max(gq_s[buf][lane]));
+    const bool any_vis = wave_has_keys && gkw_first <= t_gqmax && gkw_last >= t_dsmin;
+    const bool full = wave_keys_full && t_dsmax <= gkw_first && gkw_last <= t_gqmin;
+
+    {
+      (void)any_vis;
+#pragma unroll 1
+      for (int qb = 0; qb < 2; ++qb) {   // two 32-row blocks, one after the other
+        // ---- S = Q K^T, dP = dO V^T (one key per lane, 16 rows per lane) --------------
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int c = tid + 256 * it;
-        const int r = c >> 4, dc = c & 15;
-        bf16x8 qv = {}, dv8 = {};
-        if (q0 + r < f.Sq) {
-          const int64_t off = ((int64_t)(q0 + r) * f.Hq + h) * HD + dc * 8;
-          qv = *reinterpret_cast<const bf16x8*>(qp + off);
-          dv8 = *reinterpret_cast<const bf16x8*>(dop + off);
+        for (int kk = 0; kk < 8; ++kk) {
+          const int off = (32 * qb + r32) * QS_LD + 16 * kk + 8 * hi;
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qb[off]);
+          const bf16x8 da = *reinterpret_cast<const bf16x8*>(&Db[off]);
+          sacc = mfma32(qa, kf[kk], sacc);
+          dpacc = mfma32(da, vf[kk], dpacc);
+          if (kk & 1) __builtin_amdgcn_sched_barrier(0);
         }
-        *reinterpret_cast<bf16x8*>(&Qs[r * QS_LD + dc * 8]) = qv;
-        *reinterpret_cast<bf16x8*>(&dOs[r * QS_LD + dc * 8]) = dv8;
+        __builtin_amdgcn_sched_barrier(0);
+        if (!full) {   // wave-uniform branch: per-element mask only on boundary tiles
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          Qt[(dc * 8 + j) * QT_LD + r] = qv[j];
-          dOt[(dc * 8 + j) * QT_LD + r] = dv8[j];
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int q = 32 * qb + 8 * g4 + 4 * hi;
+            const int4 dsv = *reinterpret_cast<const int4*>(&dsq_s[buf][q]);
+            const int4 gqv = *reinterpret_cast<const int4*>(&gq_s[buf][q]);
+            const int dsa[4] = {dsv.x, dsv.y, dsv.z, dsv.w};
+            const int gqa[4] = {gqv.x, gqv.y, gqv.z, gqv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool vis = (gk >= dsa[e]) & (gk <= gqa[e]) & key_ok;
+              sacc[4 * g4 + e] = vis ? sacc[4 * g4 + e] : -INFINITY;
+            }
+          }
+        }
+        // ---- P = 2^(s*sl2 - lse2), dS = P (dP - D); row q = 32qb + 8(i/4) + 4hi + i%4
+        bf16x8 pb[2], sb[2];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int q = 32 * qb + 8 * g4 + 4 * hi;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2_s[buf][q]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&delta_s[buf][q]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * g4 + e;
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[i], sl2, -l4[e]));
+            const float ds = p * (dpacc[i] - d4[e]);
+            pb[i >> 3][i & 7] = (bf16)p;
+            sb[i >> 3][i & 7] = (bf16)ds;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- dV^T += dO^T P, dK^T += Q^T dS; k-slot j of half hi: row 16c+8(j/4)+4hi+j%4
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const int c = 2 * qb + cc;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const int off = (16 * c + tr_row) * QS_LD + 32 * db + tr_col;
+            dva[db] = mfma32(tr_operand(&Db[off], QS_LD), pb[cc], dva[db]);
+            dka[db] = mfma32(tr_operand(&Qb[off], QS_LD), sb[cc], dka[db]);
+            if (db & 1) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
+          }
+          // ---- dS^T -> LDS [key][row]: slots 4*half..+3 are rows 16c + 8*half + 4hi + 0..3
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const bf16x4 v4 = {sb[cc][4 * half], sb[cc][4 * half + 1], sb[cc][4 * half + 2],
+                               sb[cc][4 * half + 3]};
+            *reinterpret_cast<bf16x4*>(&dSt[(wave * 32 + r32) * DS_LD + 16 * c + 8 * half + 4 * hi]) = v4;
+          }
         }
       }
-      if (tid < BQ) {
-        const int r = q0 + tid;
-        const bool ok = r < f.Sq;
-        const int g = f.q_start + r;
-        lse2_s[tid] = ok ? f.lse[(int64_t)h * f.lse_ld + r] * USP_LOG2E : 0.f;
-        delta_s[tid] = ok ? a.delta[(int64_t)h * f.Sq + r] : 0.f;
-        dsq_s[tid] = !ok ? 0x7fffffff : (f.causal ? g - f.pos[g] : -0x7fffffff);
-        gq_s[tid] = !ok ? -0x7fffffff : (f.causal ? g : 0x7fffffff);
-      }
-      __syncthreads();
+    }
+    // ---- stage the next item into the other buffer; fetch the one after -------------
+    if (it + 1 < n_items) {
+      store_item(buf ^ 1);
+      if (it + 2 < n_items) load_item(it + 2);
+    }
+    __syncthreads();   // dS^T complete
 
-      // ---- S = Q K^T and dP = dO V^T (one key per lane, 16 query rows) ----------
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    // ---- dQ[rows][32 d of this wave] = dS K over the block's 128 keys -------------------
+    float* dqp = a.dq_acc + (int64_t)h * HD + 32 * wave + r32;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[r32 * QS_LD + 16 * kk + 8 * hi]);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(&dOs[r32 * QS_LD + 16 * kk + 8 * hi]);
-        sacc = mfma32(qa, kf[kk], sacc);
-        dpacc = mfma32(da, vf[kk], dpacc);
-      }
-      // every (row, key) pair of the tile visible?
-      const int dsmax = wave_max(dsq_s[r32]);
-      const int gqmin = wave_min(gq_s[r32]);
-      const bool full = keys_full && dsmax <= gk_first && gk_last <= gqmin;
-
-      bf16x8 pb[2], sb[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = 8 * (i >> 2) + 4 * hi + (i & 3);
-        const bool vis = full || (key_ok && gk >= dsq_s[q] && gk <= gq_s[q]);
-        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[i], sl2, -lse2_s[q])) : 0.f;
-        const float ds = p * (dpacc[i] - delta_s[q]);
-        pb[i >> 3][i & 7] = (bf16)p;
-        sb[i >> 3][i & 7] = (bf16)ds;
-      }
-
-      // ---- dV^T += dO^T P,  dK^T += Q^T dS (k-slot j of half hi: row 16c+8(j/4)+4hi+j%4)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const bf16* dr = &dOt[(32 * db + r32) * QT_LD + 16 * c + 4 * hi];
-          const bf16* qr = &Qt[(32 * db + r32) * QT_LD + 16 * c + 4 * hi];
-          const bf16x4 d0 = *reinterpret_cast<const bf16x4*>(dr);
-          const bf16x4 d1 = *reinterpret_cast<const bf16x4*>(dr + 8);
-          const bf16x4 q0v = *reinterpret_cast<const bf16x4*>(qr);
-          const bf16x4 q1v = *reinterpret_cast<const bf16x4*>(qr + 8);
-          const bf16x8 da = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-          const bf16x8 qa = {q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
-          dva[db] = mfma32(da, pb[c], dva[db]);
-          dka[db] = mfma32(qa, sb[c], dka[db]);
-        }
-      }
-
-      // ---- dS -> LDS as [row][key of block] ---------------------------------------
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = 8 * (i >> 2) + 4 * hi + (i & 3);
-        dSs[q * DS_LD + wave * 32 + r32] = sb[i >> 3][i & 7];
-      }
-      __syncthreads();
-
-      // ---- dQ[rows][32 d of this wave] = dS K over the block's 128 keys ------------
+    for (int qb = 0; qb < 2; ++qb) {
       f32x16 dqa = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 sa = *reinterpret_cast<const bf16x8*>(&dSs[r32 * DS_LD + 16 * kk + 8 * hi]);
-        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&Kt[(32 * wave + r32) * KT_LD + 16 * kk + 8 * hi]);
+      for (int kc = 0; kc < 8; ++kc) {
+        const bf16x8 sa = tr_operand(&dSt[(16 * kc + tr_row) * DS_LD + 32 * qb + tr_col], DS_LD);
+        const bf16x8 kb = tr_operand(&Ks[(16 * kc + tr_row) * KS_LD + 32 * wave + tr_col], KS_LD);
         dqa = mfma32(sa, kb, dqa);
+        if (kc & 1) __builtin_amdgcn_sched_barrier(0);
       }
-      float* dqp = a.dq_acc + (int64_t)h * HD + 32 * wave + r32;
+      if (q0 + 32 * qb + 32 <= f.Sq) {   // wave-uniform: every row of the block exists
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = 8 * (i >> 2) + 4 * hi + (i & 3);
-        if (q0 + q < f.Sq) atomicAdd(dqp + (int64_t)(q0 + q) * f.Hq * HD, dqa[i] * f.scale);
+        for (int i = 0; i < 16; ++i) {
+          const int q = q0 + 32 * qb + 8 * (i >> 2) + 4 * hi + (i & 3);
+          atomicAdd(dqp + (int64_t)q * f.Hq * HD, dqa[i] * f.scale);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = q0 + 32 * qb + 8 * (i >> 2) + 4 * hi + (i & 3);
+          if (q < f.Sq) atomicAdd(dqp + (int64_t)q * f.Hq * HD, dqa[i] * f.scale);
+        }
       }
     }
   }
@@ -282,8 +396,8 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   if (f.Sk > 0) {
     const int n_ktiles = (f.Sk + BKV - 1) / BKV;
     const int n_qtiles = (f.Sq + BQ - 1) / BQ;
-    hipLaunchKernelGGL(attn_bwd_main_kernel, dim3((unsigned)(n_ktiles * f.Hkv)), dim3(256), 0, stream,
-                       a, n_qtiles);
+    hipLaunchKernelGGL(attn_bwd_main_kernel, dim3((unsigned)(n_ktiles * f.Hkv)), dim3(NWB * 64), 0,
+                       stream, a, n_qtiles);
   }
   if (rows > 0) {
     const int64_t n8 = rows * HD / 8;

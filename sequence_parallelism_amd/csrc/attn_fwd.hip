@@ -8,18 +8,23 @@
 // to query gq iff gq - pos[gq] <= gk <= gq.
 //
 // bf16 / head dim 128 kernel (MFMA):
-//   * a workgroup is 4 wavefronts and owns 128 query rows of one head; each wave
+//   * a workgroup is 8 wavefronts (2 per SIMD, so one wave's softmax overlaps the
+//     other's matrix instructions) and owns 256 query rows of one head; each wave
 //     owns 32 rows and keeps its Q fragment in registers for the whole kernel;
-//   * key/value tiles of 64 keys are staged in LDS (K row-major, V transposed so
-//     that both MFMA operands are read as contiguous runs of the reduction index);
+//   * key/value tiles of 64 keys are staged row-major in double-buffered LDS; the
+//     next tile is loaded into registers while the current one is computed, so one
+//     barrier per tile suffices and HBM latency is hidden behind the MFMA work;
 //   * scores are formed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so
 //     each lane holds 16 scores of ONE query row: the row max and row sum are
 //     in-lane reductions plus one exchange with the lane 32 apart;
-//   * P^T (bf16) feeds O^T += V^T P^T directly from registers; the O^T accumulator
-//     keeps one query per lane, so the per-row rescale needs no broadcast;
-//   * exponentials are base 2 with scale*log2(e) folded into one FMA;
-//   * key tiles outside the workgroup's visible range are never visited, and tiles
-//     that are fully visible skip the per-element mask.
+//   * P^T (bf16) feeds O^T += V^T P^T directly from registers; the V^T operand is
+//     read from the row-major V tile with the gfx950 transposing LDS read
+//     (ds_read_b64_tr_b16), and the O^T accumulator keeps one query per lane;
+//   * exponentials are base 2 with scale*log2(e) folded into one FMA; the running
+//     max is only moved (and O rescaled) when it grows by more than 2^8, which
+//     keeps every P <= 256 and skips almost all rescales;
+//   * key tiles outside a wave's visible range are skipped by that wave, and tiles
+//     fully visible to a wave skip the per-element mask.
 //
 // f32 kernel (small head dims, e.g. the four-device ring example): one wavefront
 // per (query row, head), keys visited one at a time with the same running
@@ -29,13 +34,27 @@
 namespace {
 
 constexpr int HD = 128;          // head dim of the MFMA path
-constexpr int BR = 128;          // query rows per workgroup (4 waves x 32)
+constexpr int NW = 8;            // wavefronts per workgroup
+constexpr int BR = 32 * NW;      // query rows per workgroup
 constexpr int BC = 64;           // keys per LDS tile
-constexpr int KS_LD = HD + 8;    // LDS row pitch of the K tile (bf16 elements)
-constexpr int VT_LD = BC + 8;    // LDS row pitch of the V^T tile (bf16 elements)
+constexpr int KS_LD = HD + 8;    // K tile pitch (bf16): 272 B, conflict-free 16-byte reads
+constexpr int VS_LD = HD + 16;   // V tile pitch (bf16): 288 B, for the transposing reads
+constexpr float RESCALE_TH = 8.f;  // log2 of the largest P allowed before the max moves
+static_assert(BC * HD / 8 == 2 * NW * 64, "tile staging moves two 16-byte chunks per thread");
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read: within each 16-lane group, source lane s points at
+// M[k0 + s/4][m0 + 4*(s%4) .. +3] of a row-major tile; lane i receives
+// M[k0 .. k0+3][m0 + i].
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
 }
 
 __device__ __forceinline__ int wave_min(int x) {
@@ -50,10 +69,10 @@ __device__ __forceinline__ int wave_max(int x) {
 }
 
 template <bool O_F32>
-__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnArgs a, int n_qtiles) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BC * KS_LD];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[HD * VT_LD];
-  __shared__ int red[4][4];
+__global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int n_qtiles) {
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BC * KS_LD];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BC * VS_LD];
+  __shared__ int red[NW][2];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r32 = lane & 31, hi = lane >> 5;
@@ -68,8 +87,9 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnArgs a, int n_qt
   const bf16* __restrict__ kp = reinterpret_cast<const bf16*>(a.k);
   const bf16* __restrict__ vp = reinterpret_cast<const bf16*>(a.v);
 
-  // ---- visible key range of this workgroup (global token indices) ----------
-  int ds = 0x7fffffff;       // document start of this row (masked rows: +inf)
+  // ---- visible key ranges (global token indices) --------------------------------
+  // per row: [ds, gq]; per wave: [w_lo, w_hiex) plus the bounds for "fully visible"
+  int ds = 0x7fffffff;
   int lo = 0x7fffffff, hiex = -0x7fffffff, ds_max = -0x7fffffff, gq_min = 0x7fffffff;
   if (row_ok) {
     ds = a.causal ? gq - a.pos[gq] : a.k_start;
@@ -78,20 +98,22 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnArgs a, int n_qt
     ds_max = ds;
     gq_min = gq;
   }
-  lo = wave_min(lo);
-  hiex = wave_max(hiex);
-  ds_max = wave_max(ds_max);
-  gq_min = wave_min(gq_min);
-  if (lane == 0) {
-    red[wave][0] = lo; red[wave][1] = hiex; red[wave][2] = ds_max; red[wave][3] = gq_min;
-  }
+  // wave-uniform values live in scalar registers
+  const int w_lo = __builtin_amdgcn_readfirstlane(wave_min(lo));
+  const int w_hiex = __builtin_amdgcn_readfirstlane(wave_max(hiex));
+  const int w_dsmax = __builtin_amdgcn_readfirstlane(wave_max(ds_max));
+  const int w_gqmin = __builtin_amdgcn_readfirstlane(wave_min(gq_min));
+  if (lane == 0) { red[wave][0] = w_lo; red[wave][1] = w_hiex; }
   __syncthreads();
-  lo = min(min(red[0][0], red[1][0]), min(red[2][0], red[3][0]));
-  hiex = max(max(red[0][1], red[1][1]), max(red[2][1], red[3][1]));
-  ds_max = max(max(red[0][2], red[1][2]), max(red[2][2], red[3][2]));
-  gq_min = min(min(red[0][3], red[1][3]), min(red[2][3], red[3][3]));
-  const int kb = max(lo, a.k_start) - a.k_start;              // local key range [kb, ke)
-  const int ke = min(hiex, a.k_start + a.Sk) - a.k_start;
+  int g_lo = red[0][0], g_hiex = red[0][1];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) { g_lo = min(g_lo, red[w][0]); g_hiex = max(g_hiex, red[w][1]); }
+  g_lo = __builtin_amdgcn_readfirstlane(g_lo);
+  g_hiex = __builtin_amdgcn_readfirstlane(g_hiex);
+  const int kb = max(g_lo, a.k_start) - a.k_start;            // local key range [kb, ke)
+  const int ke = min(g_hiex, a.k_start + a.Sk) - a.k_start;
+  const int wkb = max(w_lo, a.k_start) - a.k_start;           // this wave's range
+  const int wke = min(w_hiex, a.k_start + a.Sk) - a.k_start;
 
   // ---- Q fragment (B operand of S^T = K Q^T): row r32, d = 16*kk + 8*hi + 0..7
   bf16x8 qf[8];
@@ -104,101 +126,141 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnArgs a, int n_qt
     }
   }
 
+  // ---- staging: 64 keys x 128 d of K and of V = 2 x 1024 16-byte chunks --------
+  // thread t moves chunks t and t + 512 of each: key = c / 16, d = 8 * (c % 16)
+  bf16x8 pk[2], pv[2];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int c = tid + NW * 64 * it;
+      const int kl = kt + (c >> 4);
+      bf16x8 z = {};
+      pk[it] = z;
+      pv[it] = z;
+      if (kl < ke) {
+        const int64_t off = ((int64_t)kl * a.Hkv + hk) * HD + (c & 15) * 8;
+        pk[it] = *reinterpret_cast<const bf16x8*>(kp + off);
+        pv[it] = *reinterpret_cast<const bf16x8*>(vp + off);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int c = tid + NW * 64 * it;
+      *reinterpret_cast<bf16x8*>(&Ks[buf][(c >> 4) * KS_LD + (c & 15) * 8]) = pk[it];
+      *reinterpret_cast<bf16x8*>(&Vs[buf][(c >> 4) * VS_LD + (c & 15) * 8]) = pv[it];
+    }
+  };
+
   const float sl2 = a.scale * USP_LOG2E;
-  float m_run = -INFINITY;    // running max, in units of log2 (scores * scale * log2 e)
+  float m_run = -INFINITY;    // running max used for P, in log2 units
   float l_run = 0.f;          // this lane's share of the running row sum
   f32x16 oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
 
-  for (int kt = kb; kt < ke; kt += BC) {
-    // ---- stage K (row-major) and V (transposed) tiles in LDS ----------------
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int c = tid + 256 * it;
-      const int key = c >> 4, dc = c & 15;
-      const int kl = kt + key;
-      bf16x8 kv = {}, vv = {};
-      if (kl < ke) {
-        const int64_t off = ((int64_t)kl * a.Hkv + hk) * HD + dc * 8;
-        kv = *reinterpret_cast<const bf16x8*>(kp + off);
-        vv = *reinterpret_cast<const bf16x8*>(vp + off);
-      }
-      *reinterpret_cast<bf16x8*>(&Ks[key * KS_LD + dc * 8]) = kv;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) Vt[(dc * 8 + j) * VT_LD + key] = vv[j];
-    }
+  // per-lane offsets of the transposing V reads (see lds_read_tr)
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int v_row = 4 * hi + (i16 >> 2);
+  const int v_col = 16 * (g16 & 1) + 4 * (i16 & 3);
+
+  if (kb < ke) {
+    load_tile(kb);
+    store_tile(0);
+    if (kb + BC < ke) load_tile(kb + BC);
     __syncthreads();
-
-    // ---- S^T tile: 64 keys x 32 queries per wave ---------------------------
-    f32x16 sacc[2];
+  }
+  int buf = 0;
+  for (int kt = kb; kt < ke; kt += BC, buf ^= 1) {
+    const bf16* Kb = Ks[buf];
+    const bf16* Vb = Vs[buf];
+    // does this wave see any key of the tile?
+    if (kt < wke && kt + BC > wkb) {
+      // ---- S^T tile: 64 keys x 32 queries -----------------------------------------
+      f32x16 sacc[2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      sacc[kb2] = f32x16{};
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        sacc[kb2] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(&Ks[(32 * kb2 + r32) * KS_LD + 16 * kk + 8 * hi]);
-        sacc[kb2] = mfma32(ka, qf[kk], sacc[kb2]);
-      }
-    }
-
-    // ---- mask, row max --------------------------------------------------------
-    const int gk0 = a.k_start + kt;
-    const bool full = (kt + BC <= ke) &&
-                      (!a.causal || (gk0 + BC - 1 <= gq_min && gk0 >= ds_max));
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = sacc[kb2][i];
-        if (!full) {
-          const int key = 32 * kb2 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          const int gk = gk0 + key;
-          const bool vis = (kt + key < ke) && (!a.causal || (gk >= ds && gk <= gq));
-          s = vis ? s : -INFINITY;
-          sacc[kb2][i] = s;
-        }
-        mloc = fmaxf(mloc, s);
-      }
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc * sl2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-
-    // ---- P = 2^(s*sl2 - m), row sum, bf16 B operands -------------------------
-    bf16x8 pb[4];
-    float psum = 0.f;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * half + j], sl2, -m_use));
-          psum += p;
-          pb[2 * kb2 + half][j] = (bf16)p;
+        for (int kk = 0; kk < 8; ++kk) {
+          const bf16x8 ka =
+              *reinterpret_cast<const bf16x8*>(&Kb[(32 * kb2 + r32) * KS_LD + 16 * kk + 8 * hi]);
+          sacc[kb2] = mfma32(ka, qf[kk], sacc[kb2]);
         }
       }
-    }
-    l_run = l_run * alpha + psum;
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- mask, row max ------------------------------------------------------------
+      const int gk0 = a.k_start + kt;
+      const bool full = (kt + BC <= ke) &&
+                        (!a.causal || (gk0 + BC - 1 <= w_gqmin && gk0 >= w_dsmax));
+      if (!full) {   // wave-uniform branch: per-element mask only on boundary tiles
+        const int klim = ke - kt;                  // keys at or past this are out of range
+        // visible: lo_k <= key <= hi_k (no int32 overflow: ds, gq, gk0 are in [0, 2^31))
+        const int lo_k = a.causal ? ds - gk0 : -BC;
+        const int hi_k = a.causal ? gq - gk0 : BC;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-
-    // ---- O^T += V^T P^T: k-slot j of lane half hi is key 16c + 8(j/4) + 4hi + j%4
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16* vr = &Vt[(32 * db + r32) * VT_LD + 16 * c + 4 * hi];
-        const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vr);
-        const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vr + 8);
-        const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        oacc[db] = mfma32(va, pb[c], oacc[db]);
+          for (int i = 0; i < 16; ++i) {
+            const int key = 32 * kb2 + 8 * (i >> 2) + 4 * hi + (i & 3);
+            const bool vis = (key < klim) & (key >= lo_k) & (key <= hi_k);
+            sacc[kb2][i] = vis ? sacc[kb2][i] : -INFINITY;
+          }
+        }
       }
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[kb2][i]);
+      }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * sl2;
+      // move the max only when it grows by more than 2^RESCALE_TH
+      const bool grow = mloc > m_run + RESCALE_TH;
+      if (__ballot(grow)) {
+        // lanes that keep their max rescale by exactly 1 (also when it is still -inf)
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mloc) : 1.f;   // 0 from -inf
+        m_run = grow ? mloc : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      // ---- P = 2^(s*sl2 - m), row sum, bf16 B operands ----------------------------
+      bf16x8 pb[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * half + j], sl2, -m_use));
+            psum += p;
+            pb[2 * kb2 + half][j] = (bf16)p;
+          }
+        }
+      }
+      l_run += psum;
+      // ---- O^T += V^T P^T: k-slot j of lane half hi is key 16c + 8(j/4) + 4hi + j%4
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16* vr = &Vb[(16 * c + v_row) * VS_LD + 32 * db + v_col];
+          const bf16x4 v0 = lds_read_tr(vr);
+          const bf16x4 v1 = lds_read_tr(vr + 8 * VS_LD);
+          const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          oacc[db] = mfma32(va, pb[c], oacc[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // bound the number of V reads in flight
+      }
+    }
+    // ---- stage the next tile into the other buffer; fetch the one after ----------
+    if (kt + BC < ke) {
+      store_tile(buf ^ 1);
+      if (kt + 2 * BC < ke) load_tile(kt + 2 * BC);
     }
     __syncthreads();
   }
@@ -280,9 +342,9 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t stream
   const int n_qtiles = (a.Sq + BR - 1) / BR;
   dim3 grid((unsigned)(n_qtiles * a.Hq));
   if (o_f32)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, grid, dim3(256), 0, stream, a, n_qtiles);
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, grid, dim3(NW * 64), 0, stream, a, n_qtiles);
   else
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, grid, dim3(256), 0, stream, a, n_qtiles);
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, grid, dim3(NW * 64), 0, stream, a, n_qtiles);
   return hipGetLastError();
 }
 
