@@ -363,3 +363,11 @@ def test_packed_doc_lengths_and_positions():
     starts = np.concatenate([[0], np.cumsum(lengths)[:-1]])
     assert np.all(pos[starts] == 0)
     assert pos.size == 131072 and pos.max() == lengths.max() - 1
+
+
+def test_causal_visible_pairs_closed_form_matches_mask_count():
+    lengths = [7, 1, 13, 4]
+    pos = inputs.position_ids(lengths)
+    S = sum(lengths)
+    brute = int(oracle.visible_mask(np.arange(S), np.arange(S), pos, True).sum())
+    assert oracle.causal_visible_pairs(lengths) == brute
