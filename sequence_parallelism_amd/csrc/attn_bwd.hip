@@ -34,11 +34,9 @@ constexpr int HD = 128;
 constexpr int NWB = 4;              // wavefronts per workgroup
 constexpr int BKV = 32 * NWB;       // keys per workgroup
 constexpr int BQ = 64;              // query rows per step
-constexpr int QS_LD = HD + 8;       // Q / dO tile pitch (bf16): 272 B
-constexpr int KS_LD = HD + 16;      // K block pitch (bf16): 288 B (transposing reads)
-constexpr int DS_LD = BQ + 8;       // dS^T tile pitch (bf16): 144 B
-static_assert(BKV * HD / 8 == 8 * NWB * 64, "K block staging moves eight 16-byte chunks per thread");
+constexpr int PF = 4;               // LDS operands kept in flight ahead of the MFMA
 static_assert((BQ * HD / 8) % (NWB * 64) == 0, "query tile staging splits evenly over threads");
+static_assert(BKV * HD / 8 == 8 * NWB * 64, "K block staging moves eight 16-byte chunks per thread");
 static_assert(BQ <= NWB * 64, "one thread per query row stages the row scalars");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -55,12 +53,34 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
   i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
   return __builtin_bit_cast(bf16x4, v);
 }
-// MFMA operand of 8 consecutive reduction indices (k-slots k0 + 8(j/4) + 4*hi + j%4)
-// for lane column m, from a row-major [k][m] tile at p = &M[k0 + rowoff][m0 + coloff].
-__device__ __forceinline__ bf16x8 tr_operand(const bf16* p, int pitch) {
-  const bf16x4 a = lds_read_tr(p);
-  const bf16x4 b = lds_read_tr(p + 8 * pitch);
+// MFMA operand of 8 reduction indices from two transposing reads (8 rows apart)
+__device__ __forceinline__ bf16x8 tr_operand(const bf16* p0, const bf16* p1) {
+  const bf16x4 a = lds_read_tr(p0);
+  const bf16x4 b = lds_read_tr(p1);
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// LDS tiles are unpadded.  A 128-element row has 16 chunks of 16 bytes, stored at
+// chunk c ^ swz16(r); a 64-element row has 8 chunks, stored at c ^ swz8(r).  With
+// these, sixteen consecutive rows read at one logical chunk, and the 4 rows x 4
+// chunks of a pair of transposing reads, touch 64 distinct banks.
+__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 1) << 2; }
+
+// N MFMAs whose operand comes from LDS: keep PF operand loads in flight ahead of
+// the MFMA that consumes them, and pin the issue order.
+template <int N, typename Load, typename Mma>
+__device__ __forceinline__ void pipelined(Load load, Mma mma) {
+  bf16x8 ops[PF];
+#pragma unroll
+  for (int i = 0; i < PF && i < N; ++i) ops[i] = load(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bf16x8 op = ops[i % PF];
+    if (i + PF < N) ops[i % PF] = load(i + PF);
+    mma(i, op);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 __device__ __forceinline__ int wave_min(int x) {
@@ -98,21 +118,20 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
 
 // ---- 2. main ----------------------------------------------------------------------
 __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, int n_qtiles) {
-  __shared__ __attribute__((aligned(16))) bf16 Qs[2][BQ * QS_LD];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[2][BQ * QS_LD];
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BKV * KS_LD];
-  __shared__ __attribute__((aligned(16))) bf16 dSt[BKV * DS_LD];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[2][BQ * HD];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[2][BQ * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Kst[BKV * HD];
+  __shared__ __attribute__((aligned(16))) bf16 dSt[BKV * BQ];
   __shared__ __attribute__((aligned(16))) float lse2_s[2][BQ];
   __shared__ __attribute__((aligned(16))) float delta_s[2][BQ];
   __shared__ __attribute__((aligned(16))) int dsq_s[2][BQ];
   __shared__ __attribute__((aligned(16))) int gq_s[2][BQ];
 
   const AttnArgs& f = a.f;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, hi = lane >> 5;
   const int g16 = lane >> 4, i16 = lane & 15;
-  const int tr_row = 4 * hi + (i16 >> 2);              // transposing-read lane offsets
-  const int tr_col = 16 * (g16 & 1) + 4 * (i16 & 3);
   const int hk = blockIdx.x % f.Hkv;
   const int k0 = (int)(blockIdx.x / f.Hkv) * BKV;      // local first key of the block
   const int kw0 = k0 + wave * 32;                       // this wave's first key
@@ -123,7 +142,6 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   const int gk_last = f.k_start + min(k0 + BKV, f.Sk) - 1;
   const int gkw_first = f.k_start + kw0;
   const int gkw_last = f.k_start + min(kw0 + 32, f.Sk) - 1;
-  const bool wave_has_keys = kw0 < f.Sk;
   const bool wave_keys_full = kw0 + 32 <= f.Sk;
   const int grp = f.Hq / f.Hkv;
   const float sl2 = f.scale * USP_LOG2E;
@@ -133,7 +151,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   const bf16* __restrict__ vp = reinterpret_cast<const bf16*>(f.v);
   const bf16* __restrict__ dop = reinterpret_cast<const bf16*>(a.dout);
 
-  // K and V fragments of this lane's key: d = 16*kk + 8*hi + 0..7
+  // K and V fragments of this lane's key (B operands of S and dP): d = 16kk + 8hi + 0..7
   bf16x8 kf[8], vf[8];
   {
     const int64_t off = ((int64_t)(key_ok ? kl : 0) * f.Hkv + hk) * HD + 8 * hi;
@@ -144,16 +162,48 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
       vf[kk] = key_ok ? *reinterpret_cast<const bf16x8*>(vp + off + 16 * kk) : z;
     }
   }
-  // the block's K, row-major in LDS (B operand of dQ = dS K via transposing reads)
+  // the block's K, row-major and swizzled in LDS, read once into the B operands of
+  // dQ = dS K: lane (d = 32*wave + r32, hi) holds K[16kc + 8(j/4) + 4hi + j%4][d]
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int c = tid + NWB * 64 * it;
-    const int key = c >> 4, dc = c & 15;
+    const int key = c >> 4, lc = c & 15;
     bf16x8 kv = {};
     if (k0 + key < f.Sk)
-      kv = *reinterpret_cast<const bf16x8*>(kp + ((int64_t)(k0 + key) * f.Hkv + hk) * HD + dc * 8);
-    *reinterpret_cast<bf16x8*>(&Ks[key * KS_LD + dc * 8]) = kv;
+      kv = *reinterpret_cast<const bf16x8*>(kp + ((int64_t)(k0 + key) * f.Hkv + hk) * HD + lc * 8);
+    *reinterpret_cast<bf16x8*>(&Kst[key * HD + ((lc ^ swz16(key)) << 3)]) = kv;
   }
+  __syncthreads();
+  // per-lane offsets of transposing reads from 128-wide rows: rows 16c + 4hi + i16/4 (+8),
+  // logical chunk 4*blk + 2(g16&1) + (i16&3)/2, half-chunk 4(i16&1)
+  auto tr16 = [&](int blk, int sec) {
+    const int row = 4 * hi + (i16 >> 2) + 8 * sec;
+    const int lc = 4 * blk + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+    return row * HD + ((lc ^ swz16(row)) << 3) + 4 * (i16 & 1);
+  };
+  bf16x8 kT[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc)
+    kT[kc] = tr_operand(&Kst[16 * kc * HD + tr16(wave, 0)], &Kst[16 * kc * HD + tr16(wave, 1)]);
+  int troff[4][2];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) { troff[db][0] = tr16(db, 0); troff[db][1] = tr16(db, 1); }
+  // 16-byte row reads of Q / dO (A operands of S, dP): row 32qb + r32, chunk 2kk + hi
+  int qoff[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) qoff[kk] = r32 * HD + (((2 * kk + hi) ^ swz16(r32)) << 3);
+  // dS^T [key][row]: transposing reads (A operand of dQ), rows 16kc + 4hi + i16/4 (+8)
+  int dsoff[2][2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int row = 4 * hi + (i16 >> 2) + 8 * sec;
+      const int lc = 4 * qb + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+      dsoff[qb][sec] = row * BQ + ((lc ^ swz8(row)) << 3) + 4 * (i16 & 1);
+    }
+  const int dsrow = (wave * 32 + r32) * BQ;                // this lane's dS^T row (its key)
+  const int dsswz = swz8(wave * 32 + r32);
 
   // ---- query tiles that can see the block: [t0, t1) ------------------------------
   int t0 = 0, t1 = n_qtiles;
@@ -206,8 +256,10 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
 #pragma unroll
     for (int u = 0; u < CHUNKS; ++u) {
       const int c = tid + NWB * 64 * u;
-      *reinterpret_cast<bf16x8*>(&Qs[buf][(c >> 4) * QS_LD + (c & 15) * 8]) = pq[u];
-      *reinterpret_cast<bf16x8*>(&dOs[buf][(c >> 4) * QS_LD + (c & 15) * 8]) = pd[u];
+      const int row = c >> 4, lc = c & 15;
+      const int off = row * HD + ((lc ^ swz16(row)) << 3);
+      *reinterpret_cast<bf16x8*>(&Qs[buf][off]) = pq[u];
+      *reinterpret_cast<bf16x8*>(&dOs[buf][off]) = pd[u];
     }
     if (tid < BQ) {
       lse2_s[buf][tid] = p_lse;
@@ -230,84 +282,83 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
     const int buf = it & 1;
     const int h = hk * grp + it / ntile;
     const int q0 = (t0 + it % ntile) * BQ;
-    __syncthreads();   // item `it` staged; dSt free
+    __syncthreads();   // item `it` staged; dS^T free
     const bf16* Qb = Qs[buf];
     const bf16* Db = dOs[buf];
 
-    // visibility of this wave's keys for the tile (wave-uniform)
+    // fully visible (tile, wave keys) pairs skip the mask (wave-uniform)
     const int t_dsmax = __builtin_amdgcn_readfirstlane(wave_max(dsq_s[buf][lane]));
-    const int t_dsmin = __builtin_amdgcn_readfirstlane(wave_min(dsq_s[buf][lane]));
     const int t_gqmin = __builtin_amdgcn_readfirstlane(wave_min(gq_s[buf][lane]));
-    const int t_gqmax = __builtin_amdgcn_readfirstlane(wave_max(gq_s[buf][lane]));
-    const bool any_vis = wave_has_keys && gkw_first <= t_gqmax && gkw_last >= t_dsmin;
     const bool full = wave_keys_full && t_dsmax <= gkw_first && gkw_last <= t_gqmin;
 
-    {
-      (void)any_vis;
 #pragma unroll 1
-      for (int qb = 0; qb < 2; ++qb) {   // two 32-row blocks, one after the other
-        // ---- S = Q K^T, dP = dO V^T (one key per lane, 16 rows per lane) --------------
-        f32x16 sacc = f32x16{}, dpacc = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const int off = (32 * qb + r32) * QS_LD + 16 * kk + 8 * hi;
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qb[off]);
-          const bf16x8 da = *reinterpret_cast<const bf16x8*>(&Db[off]);
-          sacc = mfma32(qa, kf[kk], sacc);
-          dpacc = mfma32(da, vf[kk], dpacc);
-          if (kk & 1) __builtin_amdgcn_sched_barrier(0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (!full) {   // wave-uniform branch: per-element mask only on boundary tiles
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int q = 32 * qb + 8 * g4 + 4 * hi;
-            const int4 dsv = *reinterpret_cast<const int4*>(&dsq_s[buf][q]);
-            const int4 gqv = *reinterpret_cast<const int4*>(&gq_s[buf][q]);
-            const int dsa[4] = {dsv.x, dsv.y, dsv.z, dsv.w};
-            const int gqa[4] = {gqv.x, gqv.y, gqv.z, gqv.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bool vis = (gk >= dsa[e]) & (gk <= gqa[e]) & key_ok;
-              sacc[4 * g4 + e] = vis ? sacc[4 * g4 + e] : -INFINITY;
-            }
-          }
-        }
-        // ---- P = 2^(s*sl2 - lse2), dS = P (dP - D); row q = 32qb + 8(i/4) + 4hi + i%4
-        bf16x8 pb[2], sb[2];
+    for (int qb = 0; qb < 2; ++qb) {   // two 32-row blocks, one after the other
+      // ---- S = Q K^T and dP = dO V^T (one key per lane, 16 rows per lane) ------------
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      const int rb = 32 * qb * HD;
+      pipelined<16>(
+          [&](int i) {
+            const bf16* t = (i & 1) ? Db : Qb;
+            return *reinterpret_cast<const bf16x8*>(&t[rb + qoff[i >> 1]]);
+          },
+          [&](int i, const bf16x8& op) {
+            if (i & 1) dpacc = mfma32(op, vf[i >> 1], dpacc);
+            else sacc = mfma32(op, kf[i >> 1], sacc);
+          });
+      if (!full) {   // wave-uniform branch: per-element mask only on boundary tiles
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int q = 32 * qb + 8 * g4 + 4 * hi;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2_s[buf][q]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&delta_s[buf][q]);
+          const int4 dsv = *reinterpret_cast<const int4*>(&dsq_s[buf][q]);
+          const int4 gqv = *reinterpret_cast<const int4*>(&gq_s[buf][q]);
+          const int dsa[4] = {dsv.x, dsv.y, dsv.z, dsv.w};
+          const int gqa[4] = {gqv.x, gqv.y, gqv.z, gqv.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int i = 4 * g4 + e;
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[i], sl2, -l4[e]));
-            const float ds = p * (dpacc[i] - d4[e]);
-            pb[i >> 3][i & 7] = (bf16)p;
-            sb[i >> 3][i & 7] = (bf16)ds;
+            const bool vis = (gk >= dsa[e]) & (gk <= gqa[e]) & key_ok;
+            sacc[4 * g4 + e] = vis ? sacc[4 * g4 + e] : -INFINITY;
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // ---- dV^T += dO^T P, dK^T += Q^T dS; k-slot j of half hi: row 16c+8(j/4)+4hi+j%4
+      }
+      // ---- P = 2^(s*sl2 - lse2), dS = P (dP - D); row q = 32qb + 8(i/4) + 4hi + i%4 --
+      bf16x8 pb[2], sb[2];
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const int c = 2 * qb + cc;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int q = 32 * qb + 8 * g4 + 4 * hi;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2_s[buf][q]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&delta_s[buf][q]);
 #pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const int off = (16 * c + tr_row) * QS_LD + 32 * db + tr_col;
-            dva[db] = mfma32(tr_operand(&Db[off], QS_LD), pb[cc], dva[db]);
-            dka[db] = mfma32(tr_operand(&Qb[off], QS_LD), sb[cc], dka[db]);
-            if (db & 1) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
-          }
-          // ---- dS^T -> LDS [key][row]: slots 4*half..+3 are rows 16c + 8*half + 4hi + 0..3
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g4 + e;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[i], sl2, -l4[e]));
+          const float ds = p * (dpacc[i] - d4[e]);
+          pb[i >> 3][i & 7] = (bf16)p;
+          sb[i >> 3][i & 7] = (bf16)ds;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- dV^T += dO^T P, dK^T += Q^T dS; k-slot j of half hi: row 16c+8(j/4)+4hi+j%4
+      // MFMA i: chunk cc = i / 8, head-dim block db = (i / 2) % 4, dV if i even else dK
+      pipelined<16>(
+          [&](int i) {
+            const int c = 2 * qb + (i >> 3), db = (i >> 1) & 3;
+            const bf16* t = (i & 1) ? Qb : Db;
+            return tr_operand(&t[16 * c * HD + troff[db][0]], &t[16 * c * HD + troff[db][1]]);
+          },
+          [&](int i, const bf16x8& op) {
+            const int cc = i >> 3, db = (i >> 1) & 3;
+            if (i & 1) dka[db] = mfma32(op, sb[cc], dka[db]);
+            else dva[db] = mfma32(op, pb[cc], dva[db]);
+          });
+      // ---- dS^T -> LDS [key][row]: slots 4*half..+3 are rows 16c + 8*half + 4hi + 0..3
 #pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const bf16x4 v4 = {sb[cc][4 * half], sb[cc][4 * half + 1], sb[cc][4 * half + 2],
-                               sb[cc][4 * half + 3]};
-            *reinterpret_cast<bf16x4*>(&dSt[(wave * 32 + r32) * DS_LD + 16 * c + 8 * half + 4 * hi]) = v4;
-          }
+      for (int cc = 0; cc < 2; ++cc) {
+        const int c = 2 * qb + cc;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const bf16x4 v4 = {sb[cc][4 * half], sb[cc][4 * half + 1], sb[cc][4 * half + 2],
+                             sb[cc][4 * half + 3]};
+          *reinterpret_cast<bf16x4*>(&dSt[dsrow + (((2 * c + half) ^ dsswz) << 3) + 4 * hi]) = v4;
         }
       }
     }
@@ -323,13 +374,11 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16 dqa = f32x16{};
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        const bf16x8 sa = tr_operand(&dSt[(16 * kc + tr_row) * DS_LD + 32 * qb + tr_col], DS_LD);
-        const bf16x8 kb = tr_operand(&Ks[(16 * kc + tr_row) * KS_LD + 32 * wave + tr_col], KS_LD);
-        dqa = mfma32(sa, kb, dqa);
-        if (kc & 1) __builtin_amdgcn_sched_barrier(0);
-      }
+      pipelined<8>(
+          [&](int kc) {
+            return tr_operand(&dSt[16 * kc * BQ + dsoff[qb][0]], &dSt[16 * kc * BQ + dsoff[qb][1]]);
+          },
+          [&](int kc, const bf16x8& op) { dqa = mfma32(op, kT[kc], dqa); });
       if (q0 + 32 * qb + 32 <= f.Sq) {   // wave-uniform: every row of the block exists
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
