@@ -94,6 +94,7 @@ def main():
     o_seq, dxq = torch.zeros_like(xq), torch.zeros_like(xq)
     dxk, dxv = torch.zeros_like(xk), torch.zeros_like(xv)
     ws = torch.empty(usp.bwd_workspace_bytes(S, hq, D), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(usp.fwd_workspace_bytes(S, hkv, D), dtype=torch.uint8, device=dev)
 
     vis = int(np.sum(lengths * (lengths + 1) // 2))
     fwd_flop = 4.0 * D * vis * hq
@@ -117,7 +118,7 @@ def main():
         usp.seq_to_head(xk, P, group=0, out=k)
         usp.seq_to_head(xv, P, group=0, out=v)
         mark(1)
-        usp.blockattn_fwd(q, k, v, pos, o=o, lse=lse)
+        usp.blockattn_fwd(q, k, v, pos, o=o, lse=lse, workspace=ws_f)
         mark(2)
         usp.head_to_seq(o, P, H_Q, out=o_seq, group=0)
         mark(3)

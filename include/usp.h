@@ -119,9 +119,14 @@ usp_status usp_head_to_seq_permute(void* dst, const void* src, int32_t P, int64_
  *       lse = -inf.
  * Supported: in_dtype BF16 with D = 128 (MFMA path; o_dtype BF16 or F32);
  *            in_dtype F32 with 1 <= D <= 128 (o_dtype F32).
+ * workspace: caller-owned device buffer of at least blockattn_fwd_workspace_size()
+ *   bytes, 16-byte aligned (the bf16 path keeps a head-dim-major copy of v there;
+ *   the f32 path needs none and accepts NULL).  Its contents on entry do not
+ *   matter and are clobbered; it must not overlap any other argument.
  * Alignment: bf16 q, k, v, o 16-byte aligned.
  * Errors: NULL pointers (position_ids only when causal); Sq, Sk < 0; Hq, Hkv < 1;
- * Hq % Hkv; lse_ld < Sq; q_start, k_start < 0; unsupported dtype / D; misaligned.
+ * Hq % Hkv; lse_ld < Sq; q_start, k_start < 0; unsupported dtype / D; misaligned;
+ * workspace too small.
  * Sq == 0 or Sk == 0 is valid (Sk == 0 writes o = 0, lse = -inf).
  * ------------------------------------------------------------------------- */
 usp_status blockattn_fwd(const void* q, const void* k, const void* v,
@@ -129,7 +134,11 @@ usp_status blockattn_fwd(const void* q, const void* k, const void* v,
                          const int32_t* position_ids, int64_t q_start, int64_t k_start,
                          int32_t causal, float softmax_scale, usp_dtype in_dtype,
                          void* o, usp_dtype o_dtype, float* lse, int64_t lse_ld,
-                         void* stream);
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace blockattn_fwd needs for these sizes (0 for F32). */
+usp_status blockattn_fwd_workspace_size(int64_t Sk, int32_t Hkv, int32_t D, usp_dtype in_dtype,
+                                        size_t* bytes);
 
 /* Bytes of device workspace blockattn_bwd needs for these sizes. */
 usp_status blockattn_bwd_workspace_size(int64_t Sq, int32_t Hq, int32_t D, size_t* bytes);

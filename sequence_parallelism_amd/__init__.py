@@ -32,7 +32,10 @@ SIGNATURES = {
                                                ctypes.c_int, _c_int32, _vp]),
     "blockattn_fwd": (ctypes.c_int, [_vp, _vp, _vp, _c_int64, _c_int64, _c_int32, _c_int32,
                                      _c_int32, _vp, _c_int64, _c_int64, _c_int32, _c_float,
-                                     ctypes.c_int, _vp, ctypes.c_int, _vp, _c_int64, _vp]),
+                                     ctypes.c_int, _vp, ctypes.c_int, _vp, _c_int64, _vp,
+                                     ctypes.c_size_t, _vp]),
+    "blockattn_fwd_workspace_size": (ctypes.c_int, [_c_int64, _c_int32, _c_int32, ctypes.c_int,
+                                                    ctypes.POINTER(ctypes.c_size_t)]),
     "blockattn_bwd_workspace_size": (ctypes.c_int, [_c_int64, _c_int32, _c_int32,
                                                     ctypes.POINTER(ctypes.c_size_t)]),
     "blockattn_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_int64, _vp, _c_int64, _c_int64,
@@ -142,8 +145,16 @@ def head_to_seq(src, P, H, out=None, group=-1, stream=None):
 
 # ---- attention --------------------------------------------------------------------
 
+def fwd_workspace_bytes(Sk, Hkv, D, dtype_code=BF16):
+    lib = load()
+    n = ctypes.c_size_t(0)
+    _check("blockattn_fwd_workspace_size",
+           lib.blockattn_fwd_workspace_size(Sk, Hkv, D, dtype_code, ctypes.byref(n)))
+    return n.value
+
+
 def blockattn_fwd(q, k, v, position_ids=None, q_start=0, k_start=0, causal=True, scale=None,
-                  o=None, lse=None, o_dtype=None, stream=None):
+                  o=None, lse=None, o_dtype=None, workspace=None, stream=None):
     """q [Sq][Hq][D], k, v [Sk][Hkv][D] -> (o [Sq][Hq][D], lse [Hq][Sq] float32)."""
     import torch
     lib = load()
@@ -161,10 +172,15 @@ def blockattn_fwd(q, k, v, position_ids=None, q_start=0, k_start=0, causal=True,
         _need(position_ids, "position_ids")
         if position_ids.dtype != torch.int32:
             raise TypeError("position_ids must be int32")
+    need = fwd_workspace_bytes(Sk, Hkv, D, _dtype_code(q))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("blockattn_fwd",
            lib.blockattn_fwd(_ptr(q), _ptr(k), _ptr(v), Sq, Sk, Hq, Hkv, D, _ptr(position_ids),
                              q_start, k_start, int(bool(causal)), scale, _dtype_code(q),
-                             _ptr(o), _dtype_code(o), _ptr(lse), lse.stride(0), _stream(stream)))
+                             _ptr(o), _dtype_code(o), _ptr(lse), lse.stride(0),
+                             _ptr(workspace), ws_bytes, _stream(stream)))
     return o, lse
 
 
@@ -215,4 +231,4 @@ def lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
 
 
 __all__ = ["load", "seq_to_head", "head_to_seq", "blockattn_fwd", "blockattn_bwd",
-           "bwd_workspace_bytes", "lse_merge", "UspError", "BF16", "F32", "SIGNATURES"]
+           "fwd_workspace_bytes", "bwd_workspace_bytes", "lse_merge", "UspError", "BF16", "F32", "SIGNATURES"]

@@ -8,22 +8,27 @@
 // to query gq iff gq - pos[gq] <= gk <= gq.
 //
 // bf16 / head dim 128 kernel (MFMA):
-//   * a workgroup is 8 wavefronts (2 per SIMD, so one wave's softmax overlaps the
-//     other's matrix instructions) and owns 256 query rows of one head; each wave
-//     owns 32 rows and keeps its Q fragment in registers for the whole kernel;
-//   * key/value tiles of 64 keys are staged row-major in double-buffered LDS; the
-//     next tile is loaded into registers while the current one is computed, so one
-//     barrier per tile suffices and HBM latency is hidden behind the MFMA work;
+//   * a workgroup is 8 wavefronts (2 per SIMD) and owns 256 query rows of one head;
+//     each wave owns 32 rows and keeps its Q fragment in registers;
+//   * key tiles of 64 keys are staged in double-buffered LDS: K row-major, and V
+//     from its head-dim-major copy (V^T, made once per call by transpose.hip), so
+//     every MFMA operand taken from LDS is ONE 16-byte read (LDS instruction issue,
+//     not bytes, is what limits narrower reads on gfx950).  The next tile is
+//     fetched into registers while the current one is computed, so one barrier per
+//     tile suffices and HBM latency is hidden behind the MFMA work; operand reads
+//     run four MFMAs ahead of their use;
+//   * LDS rows are unpadded with XOR-swizzled 16-byte chunks: 16 lanes reading 16
+//     consecutive rows at one logical chunk hit all 64 banks once;
 //   * scores are formed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so
 //     each lane holds 16 scores of ONE query row: the row max and row sum are
 //     in-lane reductions plus one exchange with the lane 32 apart;
-//   * P^T (bf16) feeds O^T += V^T P^T directly from registers; the V^T operand is
-//     read from the row-major V tile with the gfx950 transposing LDS read
-//     (ds_read_b64_tr_b16), and the O^T accumulator keeps one query per lane;
+//   * P^T (bf16) feeds O^T += V^T P^T directly from registers (the token order of
+//     V^T inside each 16-token group matches the lanes' score slots), and the O^T
+//     accumulator keeps one query per lane, so the per-row rescale needs no
+//     broadcast;
 //   * exponentials are base 2 with scale*log2(e) folded into one FMA; the running
-//     max is only moved (and O rescaled) when it grows by more than 2^8, which
-//     keeps every P <= 256 and skips almost all rescales;
-//   * key tiles outside a wave's visible range are skipped by that wave, and tiles
+//     max is only moved (and O rescaled) when it grows by more than 2^8;
+//   * key tiles outside the workgroup's visible range are never visited, and tiles
 //     fully visible to a wave skip the per-element mask.
 //
 // f32 kernel (small head dims, e.g. the four-device ring example): one wavefront
@@ -37,25 +42,19 @@ constexpr int HD = 128;          // head dim of the MFMA path
 constexpr int NW = 8;            // wavefronts per workgroup
 constexpr int BR = 32 * NW;      // query rows per workgroup
 constexpr int BC = 64;           // keys per LDS tile
-constexpr int KS_LD = HD + 8;    // K tile pitch (bf16): 272 B, conflict-free 16-byte reads
-constexpr int VS_LD = HD + 16;   // V tile pitch (bf16): 288 B, for the transposing reads
+constexpr int PF = 4;            // LDS operand reads in flight ahead of their MFMA
 constexpr float RESCALE_TH = 8.f;  // log2 of the largest P allowed before the max moves
-static_assert(BC * HD / 8 == 2 * NW * 64, "tile staging moves two 16-byte chunks per thread");
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+constexpr int CH = BC * HD / 8 / (NW * 64);   // 16-byte chunks per thread per K (V^T) tile
+static_assert(CH * NW * 64 == BC * HD / 8, "tile staging splits evenly over threads");
+constexpr int NXCD = 8;          // MI355X dispatches workgroup i to XCD i % 8
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Transposing LDS read: within each 16-lane group, source lane s points at
-// M[k0 + s/4][m0 + 4*(s%4) .. +3] of a row-major tile; lane i receives
-// M[k0 .. k0+3][m0 + i].
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
-  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
+// Swizzles of 16-byte chunks: rows of 128 bf16 (16 chunks) and of 64 bf16 (8 chunks).
+__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ int wave_min(int x) {
 #pragma unroll
@@ -68,16 +67,39 @@ __device__ __forceinline__ int wave_max(int x) {
   return x;
 }
 
+// N MFMAs whose A operand comes from LDS: PF reads stay in flight ahead of use.
+template <int N, typename Load, typename Mma>
+__device__ __forceinline__ void pipelined(Load load, Mma mma) {
+  bf16x8 ops[PF];
+#pragma unroll
+  for (int i = 0; i < PF && i < N; ++i) ops[i] = load(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bf16x8 op = ops[i % PF];
+    if (i + PF < N) ops[i % PF] = load(i + PF);
+    mma(i, op);
+    __builtin_amdgcn_sched_barrier(0);   // keep PF reads in flight: the compiler would
+                                          // otherwise pull them next to their MFMA
+  }
+}
+
 template <bool O_F32>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int n_qtiles) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BC * KS_LD];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BC * VS_LD];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BC * HD];    // [key][d]
+  __shared__ __attribute__((aligned(16))) bf16 Vt[2][HD * BC];    // [d][key position]
   __shared__ int red[NW][2];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, hi = lane >> 5;
-  const int h = blockIdx.x % a.Hq;
-  const int qt = n_qtiles - 1 - (int)(blockIdx.x / a.Hq);   // longest causal rows first
+  // XCD-aware order: the workgroups an XCD runs back to back are the query heads
+  // of one query tile (heads sharing a key/value head are adjacent), tiles taken
+  // every NXCD-th from the longest causal rows down, so concurrent workgroups on an
+  // XCD read the same key/value tiles from its L2 and every XCD gets a fair share.
+  const int xcd = blockIdx.x % NXCD, j = blockIdx.x / NXCD;
+  const int h = j % a.Hq;
+  const int qt = n_qtiles - 1 - ((j / a.Hq) * NXCD + xcd);
+  if (qt < 0) return;                                       // grid padding (whole workgroup)
   const int hk = h / (a.Hq / a.Hkv);
   const int row = qt * BR + wave * 32 + r32;
   const bool row_ok = row < a.Sq;
@@ -85,10 +107,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
 
   const bf16* __restrict__ qp = reinterpret_cast<const bf16*>(a.q);
   const bf16* __restrict__ kp = reinterpret_cast<const bf16*>(a.k);
-  const bf16* __restrict__ vp = reinterpret_cast<const bf16*>(a.v);
+  const bf16* __restrict__ vtp = reinterpret_cast<const bf16*>(a.vt) + (int64_t)hk * HD * a.vt_ld;
 
   // ---- visible key ranges (global token indices) --------------------------------
-  // per row: [ds, gq]; per wave: [w_lo, w_hiex) plus the bounds for "fully visible"
   int ds = 0x7fffffff;
   int lo = 0x7fffffff, hiex = -0x7fffffff, ds_max = -0x7fffffff, gq_min = 0x7fffffff;
   if (row_ok) {
@@ -110,10 +131,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   for (int w = 1; w < NW; ++w) { g_lo = min(g_lo, red[w][0]); g_hiex = max(g_hiex, red[w][1]); }
   g_lo = __builtin_amdgcn_readfirstlane(g_lo);
   g_hiex = __builtin_amdgcn_readfirstlane(g_hiex);
-  const int kb = max(g_lo, a.k_start) - a.k_start;            // local key range [kb, ke)
+  // local key range [kb, ke); tiles start on 16-key groups (the V^T slot order)
   const int ke = min(g_hiex, a.k_start + a.Sk) - a.k_start;
-  const int wkb = max(w_lo, a.k_start) - a.k_start;           // this wave's range
-  const int wke = min(w_hiex, a.k_start + a.Sk) - a.k_start;
+  const int kb = (max(g_lo, a.k_start) - a.k_start) & ~15;
 
   // ---- Q fragment (B operand of S^T = K Q^T): row r32, d = 16*kk + 8*hi + 0..7
   bf16x8 qf[8];
@@ -126,30 +146,26 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
     }
   }
 
-  // ---- staging: 64 keys x 128 d of K and of V = 2 x 1024 16-byte chunks --------
-  // thread t moves chunks t and t + 512 of each: key = c / 16, d = 8 * (c % 16)
-  bf16x8 pk[2], pv[2];
+  // ---- staging: K tile [64 keys][128] and V^T tile [128][64 positions] ----------
+  bf16x8 pk[CH], pv[CH];
   auto load_tile = [&](int kt) {
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int c = tid + NW * 64 * it;
-      const int kl = kt + (c >> 4);
-      bf16x8 z = {};
-      pk[it] = z;
-      pv[it] = z;
-      if (kl < ke) {
-        const int64_t off = ((int64_t)kl * a.Hkv + hk) * HD + (c & 15) * 8;
-        pk[it] = *reinterpret_cast<const bf16x8*>(kp + off);
-        pv[it] = *reinterpret_cast<const bf16x8*>(vp + off);
-      }
+    for (int u = 0; u < CH; ++u) {
+      const int c = tid + NW * 64 * u;
+      // K: key kt + c/16 (clamped to a real row; the mask zeroes it), chunk c%16
+      const int kl = min(kt + (c >> 4), a.Sk - 1);
+      pk[u] = *reinterpret_cast<const bf16x8*>(kp + ((int64_t)kl * a.Hkv + hk) * HD + (c & 15) * 8);
+      // V^T: row d = c/8, positions kt + 8*(c%8) .. +7 (the padded copy covers them)
+      pv[u] = *reinterpret_cast<const bf16x8*>(vtp + (int64_t)(c >> 3) * a.vt_ld + kt + (c & 7) * 8);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int c = tid + NW * 64 * it;
-      *reinterpret_cast<bf16x8*>(&Ks[buf][(c >> 4) * KS_LD + (c & 15) * 8]) = pk[it];
-      *reinterpret_cast<bf16x8*>(&Vs[buf][(c >> 4) * VS_LD + (c & 15) * 8]) = pv[it];
+    for (int u = 0; u < CH; ++u) {
+      const int c = tid + NW * 64 * u;
+      const int kr = c >> 4, kc = c & 15, vr = c >> 3, vc = c & 7;
+      *reinterpret_cast<bf16x8*>(&Ks[buf][kr * HD + ((kc ^ swz16(kr)) << 3)]) = pk[u];
+      *reinterpret_cast<bf16x8*>(&Vt[buf][vr * BC + ((vc ^ swz8(vr)) << 3)]) = pv[u];
     }
   };
 
@@ -160,10 +176,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
 
-  // per-lane offsets of the transposing V reads (see lds_read_tr)
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const int v_row = 4 * hi + (i16 >> 2);
-  const int v_col = 16 * (g16 & 1) + 4 * (i16 & 3);
+  // per-lane element offsets inside the tiles (swizzled)
+  //   K (A operand of S^T): row 32*kb2 + r32, logical chunk 2*kk + hi
+  //   V^T (A operand of O^T): row 32*db + r32, logical chunk 2c + hi (positions
+  //   16c + 8hi .. +7 = the lane half's eight key slots of chunk c)
+  int koff[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) koff[kk] = r32 * HD + (((2 * kk + hi) ^ swz16(r32)) << 3);
+  int voff[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) voff[c] = r32 * BC + (((2 * c + hi) ^ swz8(r32)) << 3);
 
   if (kb < ke) {
     load_tile(kb);
@@ -174,89 +196,67 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   int buf = 0;
   for (int kt = kb; kt < ke; kt += BC, buf ^= 1) {
     const bf16* Kb = Ks[buf];
-    const bf16* Vb = Vs[buf];
-    // does this wave see any key of the tile?
-    if (kt < wke && kt + BC > wkb) {
-      // ---- S^T tile: 64 keys x 32 queries -----------------------------------------
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        sacc[kb2] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const bf16x8 ka =
-              *reinterpret_cast<const bf16x8*>(&Kb[(32 * kb2 + r32) * KS_LD + 16 * kk + 8 * hi]);
-          sacc[kb2] = mfma32(ka, qf[kk], sacc[kb2]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- mask, row max ------------------------------------------------------------
-      const int gk0 = a.k_start + kt;
-      const bool full = (kt + BC <= ke) &&
-                        (!a.causal || (gk0 + BC - 1 <= w_gqmin && gk0 >= w_dsmax));
-      if (!full) {   // wave-uniform branch: per-element mask only on boundary tiles
-        const int klim = ke - kt;                  // keys at or past this are out of range
-        // visible: lo_k <= key <= hi_k (no int32 overflow: ds, gq, gk0 are in [0, 2^31))
-        const int lo_k = a.causal ? ds - gk0 : -BC;
-        const int hi_k = a.causal ? gq - gk0 : BC;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = 32 * kb2 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            const bool vis = (key < klim) & (key >= lo_k) & (key <= hi_k);
-            sacc[kb2][i] = vis ? sacc[kb2][i] : -INFINITY;
-          }
-        }
-      }
-      float mloc = -INFINITY;
+    const bf16* Vb = Vt[buf];
+    // ---- S^T tile: 64 keys x 32 queries (MFMA i: key block i%2, d chunk i/2) ------
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    pipelined<16>([&](int i) { return *reinterpret_cast<const bf16x8*>(&Kb[32 * (i & 1) * HD + koff[i >> 1]]); },
+                  [&](int i, const bf16x8& op) { sacc[i & 1] = mfma32(op, qf[i >> 1], sacc[i & 1]); });
+    // ---- mask, row max ------------------------------------------------------------
+    const int gk0 = a.k_start + kt;
+    const bool full = (kt + BC <= ke) && (kt >= 0) &&
+                      (!a.causal || (gk0 + BC - 1 <= w_gqmin && gk0 >= w_dsmax));
+    if (!full) {   // wave-uniform branch: per-element mask only on boundary tiles
+      const int klim = ke - kt;
+      // visible: lo_k <= key <= hi_k (no int32 overflow: ds, gq, gk0 are in [0, 2^31))
+      const int lo_k = a.causal ? max(ds - gk0, kb - kt) : kb - kt;
+      const int hi_k = a.causal ? gq - gk0 : BC;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[kb2][i]);
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * sl2;
-      // move the max only when it grows by more than 2^RESCALE_TH
-      const bool grow = mloc > m_run + RESCALE_TH;
-      if (__ballot(grow)) {
-        // lanes that keep their max rescale by exactly 1 (also when it is still -inf)
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mloc) : 1.f;   // 0 from -inf
-        m_run = grow ? mloc : m_run;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      // ---- P = 2^(s*sl2 - m), row sum, bf16 B operands ----------------------------
-      bf16x8 pb[4];
-      float psum = 0.f;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * half + j], sl2, -m_use));
-            psum += p;
-            pb[2 * kb2 + half][j] = (bf16)p;
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int key = 32 * kb2 + 8 * (i >> 2) + 4 * hi + (i & 3);
+          const bool vis = (key < klim) & (key >= lo_k) & (key <= hi_k);
+          sacc[kb2][i] = vis ? sacc[kb2][i] : -INFINITY;
         }
-      }
-      l_run += psum;
-      // ---- O^T += V^T P^T: k-slot j of lane half hi is key 16c + 8(j/4) + 4hi + j%4
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const bf16* vr = &Vb[(16 * c + v_row) * VS_LD + 32 * db + v_col];
-          const bf16x4 v0 = lds_read_tr(vr);
-          const bf16x4 v1 = lds_read_tr(vr + 8 * VS_LD);
-          const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          oacc[db] = mfma32(va, pb[c], oacc[db]);
-        }
-        __builtin_amdgcn_sched_barrier(0);   // bound the number of V reads in flight
       }
     }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[kb2][i]);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * sl2;
+    // move the max only when it grows by more than 2^RESCALE_TH
+    const bool grow = mloc > m_run + RESCALE_TH;
+    if (__ballot(grow)) {
+      // lanes that keep their max rescale by exactly 1 (also when it is still -inf)
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mloc) : 1.f;   // 0 from -inf
+      m_run = grow ? mloc : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    // ---- P = 2^(s*sl2 - m), row sum, bf16 B operands ------------------------------
+    bf16x8 pb[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * half + j], sl2, -m_use));
+          psum += p;
+          pb[2 * kb2 + half][j] = (bf16)p;
+        }
+      }
+    }
+    l_run += psum;
+    // ---- O^T += V^T P^T (MFMA i: key chunk c = i/4, head-dim block db = i%4) --------
+    pipelined<16>([&](int i) { return *reinterpret_cast<const bf16x8*>(&Vb[32 * (i & 3) * BC + voff[i >> 2]]); },
+                  [&](int i, const bf16x8& op) { oacc[i & 3] = mfma32(op, pb[i >> 2], oacc[i & 3]); });
     // ---- stage the next tile into the other buffer; fetch the one after ----------
     if (kt + BC < ke) {
       store_tile(buf ^ 1);
@@ -337,10 +337,20 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
+size_t attn_fwd_workspace_bytes(int64_t Sk, int32_t Hkv, int32_t D, int bf16_path) {
+  if (!bf16_path) return 0;
+  return (size_t)Hkv * D * transpose_perm16_padded_len(Sk) * sizeof(bf16);
+}
+
+// a.vt must point at a workspace of attn_fwd_workspace_bytes; it is filled here.
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t stream) {
   if (a.Sq == 0) return hipSuccess;
+  if (a.Sk > 0) {
+    hipError_t e = launch_transpose_perm16(a.v, a.Sk, a.Hkv, const_cast<void*>(a.vt), stream);
+    if (e != hipSuccess) return e;
+  }
   const int n_qtiles = (a.Sq + BR - 1) / BR;
-  dim3 grid((unsigned)(n_qtiles * a.Hq));
+  dim3 grid((unsigned)(((n_qtiles + NXCD - 1) / NXCD) * NXCD * a.Hq));
   if (o_f32)
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, grid, dim3(NW * 64), 0, stream, a, n_qtiles);
   else

@@ -43,8 +43,11 @@ struct AttnArgs {
   int32_t q_start, k_start;
   int32_t causal;
   float scale;
+  const void* vt;      // bf16 path: V in head-dim-major layout (see transpose.hip)
+  int64_t vt_ld;       // its padded token length
 };
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t s);
+size_t attn_fwd_workspace_bytes(int64_t Sk, int32_t Hkv, int32_t D, int bf16_path);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t s);
 
 struct AttnBwdArgs {
@@ -58,6 +61,11 @@ struct AttnBwdArgs {
 };
 size_t attn_bwd_workspace_bytes(int64_t Sq, int32_t Hq, int32_t D);
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s);
+
+// Y[h][d][p] = X[tok(p)][h][d] over a padded token axis, 16-token groups permuted
+// to MFMA slot order (transpose.hip); D = 128, bf16.
+int64_t transpose_perm16_padded_len(int64_t S);
+hipError_t launch_transpose_perm16(const void* x, int64_t S, int32_t H, void* y, hipStream_t s);
 
 struct MergeArgs {
   void* o_acc;

@@ -72,9 +72,9 @@ def test_permute_validation(lib, fn):
 
 
 def _fwd(lib, q=A, k=A, v=A, Sq=256, Sk=256, Hq=4, Hkv=1, D=128, pos=A, qs=0, ks=0, causal=1,
-         dt=0, o=A, odt=0, lse=A, ld=256):
+         dt=0, o=A, odt=0, lse=A, ld=256, ws=A, ws_bytes=1 << 30):
     return lib.blockattn_fwd(q, k, v, Sq, Sk, Hq, Hkv, D, pos, qs, ks, causal, 0.1, dt, o, odt,
-                             lse, ld, None)
+                             lse, ld, ws, ws_bytes, None)
 
 
 def test_fwd_validation(lib):
@@ -91,6 +91,12 @@ def test_fwd_validation(lib):
     assert _fwd(lib, dt=1, odt=0, D=16) == DTYPE        # f32 input needs f32 output
     assert _fwd(lib, q=A + 2) == MISAL
     assert _fwd(lib, qs=(1 << 31) - 10) == UNSUP        # global index past int32
+    n = ctypes.c_size_t(0)
+    assert lib.blockattn_fwd_workspace_size(256, 1, 128, 0, ctypes.byref(n)) == OK and n.value > 0
+    assert _fwd(lib, ws_bytes=n.value - 1) == WS
+    assert _fwd(lib, ws=None) == NULLP
+    assert _fwd(lib, ws=A + 8) == MISAL
+    assert lib.blockattn_fwd_workspace_size(256, 1, 16, 1, ctypes.byref(n)) == OK and n.value == 0
 
 
 def test_bwd_validation(lib):
