@@ -93,7 +93,7 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     o_seq, dxq = torch.zeros_like(xq), torch.zeros_like(xq)
     dxk, dxv = torch.zeros_like(xk), torch.zeros_like(xv)
-    ws = torch.empty(usp.bwd_workspace_bytes(S, hq, D), dtype=torch.uint8, device=dev)
+    ws = torch.empty(usp.bwd_workspace_bytes(S, S, hq, hkv, D), dtype=torch.uint8, device=dev)
     ws_f = torch.empty(usp.fwd_workspace_bytes(S, hkv, D), dtype=torch.uint8, device=dev)
 
     vis = int(np.sum(lengths * (lengths + 1) // 2))

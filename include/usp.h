@@ -141,7 +141,8 @@ usp_status blockattn_fwd_workspace_size(int64_t Sk, int32_t Hkv, int32_t D, usp_
                                         size_t* bytes);
 
 /* Bytes of device workspace blockattn_bwd needs for these sizes. */
-usp_status blockattn_bwd_workspace_size(int64_t Sq, int32_t Hq, int32_t D, size_t* bytes);
+usp_status blockattn_bwd_workspace_size(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D,
+                                        size_t* bytes);
 
 /* ---------------------------------------------------------------------------
  * Backward of blockattn_fwd (the pages are silent on the backward pass; this is

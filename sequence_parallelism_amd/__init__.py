@@ -36,8 +36,8 @@ SIGNATURES = {
                                      ctypes.c_size_t, _vp]),
     "blockattn_fwd_workspace_size": (ctypes.c_int, [_c_int64, _c_int32, _c_int32, ctypes.c_int,
                                                     ctypes.POINTER(ctypes.c_size_t)]),
-    "blockattn_bwd_workspace_size": (ctypes.c_int, [_c_int64, _c_int32, _c_int32,
-                                                    ctypes.POINTER(ctypes.c_size_t)]),
+    "blockattn_bwd_workspace_size": (ctypes.c_int, [_c_int64, _c_int64, _c_int32, _c_int32,
+                                                    _c_int32, ctypes.POINTER(ctypes.c_size_t)]),
     "blockattn_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_int64, _vp, _c_int64, _c_int64,
                                      _c_int32, _c_int32, _c_int32, _vp, _c_int64, _c_int64,
                                      _c_int32, _c_float, ctypes.c_int, _vp, _vp, _vp, _vp,
@@ -184,11 +184,11 @@ def blockattn_fwd(q, k, v, position_ids=None, q_start=0, k_start=0, causal=True,
     return o, lse
 
 
-def bwd_workspace_bytes(Sq, Hq, D):
+def bwd_workspace_bytes(Sq, Sk, Hq, Hkv, D):
     lib = load()
     n = ctypes.c_size_t(0)
     _check("blockattn_bwd_workspace_size",
-           lib.blockattn_bwd_workspace_size(Sq, Hq, D, ctypes.byref(n)))
+           lib.blockattn_bwd_workspace_size(Sq, Sk, Hq, Hkv, D, ctypes.byref(n)))
     return n.value
 
 
@@ -205,7 +205,7 @@ def blockattn_bwd(q, k, v, o, lse, dout, position_ids=None, q_start=0, k_start=0
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = bwd_workspace_bytes(Sq, Hq, D)
+    need = bwd_workspace_bytes(Sq, Sk, Hq, Hkv, D)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check("blockattn_bwd",

@@ -5,27 +5,30 @@
 //   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q,
 // with dK, dV of a key/value head summed over the query heads that share it.
 //
-// Three kernels:
-//   1. pre:  D_i for every (row, head) and zeroing of the fp32 dQ accumulator;
-//   2. main: a workgroup owns 128 keys of one key/value head (32 per wave; K and V
-//            of those keys are MFMA B-operand fragments in registers, and the
-//            block's K is also staged row-major in LDS for dQ) and walks the
-//            query tiles that can see them, 64 rows at a time, for every query
-//            head of the group.  Query / dO tiles are double-buffered in LDS and
-//            the next one is fetched into registers while the current one is
-//            computed.  Per tile each wave recomputes S = Q K^T and dP = dO V^T
-//            with v_mfma_f32_32x32x16_bf16 (one key per lane, query rows in
-//            registers), forms P and dS in registers, and accumulates
-//            dV^T += dO^T P and dK^T += Q^T dS in registers, reading the
-//            transposed operands with the gfx950 transposing LDS read.  dS^T goes
-//            to LDS once; each wave then forms dQ for 32 of the 128 head-dim
-//            columns over the block's 128 keys and adds it to the fp32
-//            accumulator with atomics that are coalesced along the head dim;
-//   3. post: dQ accumulator -> bf16.
+// Kernels, in stream order:
+//   1. pre:       D_i for every (row, head) and zeroing of the fp32 dQ accumulator;
+//   2. transpose: head-dim-major copies of q, dout and k in the workspace
+//                 (transpose.hip), so that every MFMA operand read from LDS below
+//                 is ONE 16-byte read (narrower LDS reads cost as much issue time
+//                 as 16-byte ones on gfx950);
+//   3. main:      a workgroup owns 128 keys of one key/value head (32 per wave; K
+//                 and V of the lane's key are B operands in registers, and the K
+//                 operand of dQ = dS K for this wave's 32 head-dim columns too) and
+//                 walks the 64-row query tiles that can see the block, for every
+//                 query head of the group.  A tile is Q and dO row-major plus Q^T
+//                 and dO^T head-dim-major (64 KB), brought into double-buffered LDS
+//                 by LDS-DMA one tile ahead.  Per tile each wave forms S = Q K^T
+//                 and dP = dO V^T with v_mfma_f32_32x32x16_bf16 (one key per lane,
+//                 16 rows per lane), P and dS in registers, and accumulates
+//                 dV^T += dO^T P and dK^T += Q^T dS; dS goes to LDS once; each wave
+//                 then forms dQ for 32 of the 128 head-dim columns over the block's
+//                 128 keys and adds it to the fp32 accumulator with atomics that
+//                 are coalesced along the head dim (issued one tile later, so the
+//                 wait for the next tile's DMA never waits on them);
+//   4. post:      dQ accumulator -> bf16.
 // Query tiles that cannot see the key block are not visited (the first visible
 // tile follows from the block's first key, the last from a binary search over
-// document starts); waves whose keys a tile cannot see skip its matrix work, and
-// fully visible (tile, wave) pairs skip the per-element mask.
+// document starts), and fully visible (tile, wave) pairs skip the per-element mask.
 #include "common.h"
 
 namespace {
@@ -34,41 +37,38 @@ constexpr int HD = 128;
 constexpr int NWB = 4;              // wavefronts per workgroup
 constexpr int BKV = 32 * NWB;       // keys per workgroup
 constexpr int BQ = 64;              // query rows per step
-constexpr int PF = 4;               // LDS operands kept in flight ahead of the MFMA
-static_assert((BQ * HD / 8) % (NWB * 64) == 0, "query tile staging splits evenly over threads");
-static_assert(BKV * HD / 8 == 8 * NWB * 64, "K block staging moves eight 16-byte chunks per thread");
+constexpr int PF = 4;               // LDS operand reads in flight ahead of their MFMA
+constexpr int TILE = BQ * HD;       // elements of one staged tile (16 KB)
+static_assert(TILE / 8 == 4 * NWB * 64, "a staged tile is four 64-lane DMA loads per wave");
 static_assert(BQ <= NWB * 64, "one thread per query row stages the row scalars");
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Transposing LDS read: within each 16-lane group, source lane s points at
-// M[k0 + s/4][m0 + 4*(s%4) .. +3] of a row-major tile; lane i receives
-// M[k0 .. k0+3][m0 + i].
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
-  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
-// MFMA operand of 8 reduction indices from two transposing reads (8 rows apart)
-__device__ __forceinline__ bf16x8 tr_operand(const bf16* p0, const bf16* p1) {
-  const bf16x4 a = lds_read_tr(p0);
-  const bf16x4 b = lds_read_tr(p1);
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// LDS tiles are unpadded.  A 128-element row has 16 chunks of 16 bytes, stored at
-// chunk c ^ swz16(r); a 64-element row has 8 chunks, stored at c ^ swz8(r).  With
-// these, sixteen consecutive rows read at one logical chunk, and the 4 rows x 4
-// chunks of a pair of transposing reads, touch 64 distinct banks.
+// LDS tiles are unpadded; 16-byte chunk c of row r is stored at c ^ swz(r).  With
+// these, 16 lanes reading 16 consecutive rows at one logical chunk touch all 64
+// banks once.  Rows of 128 bf16 have 16 chunks, rows of 64 bf16 have 8.
 __device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 1) << 2; }
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
-// N MFMAs whose operand comes from LDS: keep PF operand loads in flight ahead of
-// the MFMA that consumes them, and pin the issue order.
+// Position of token offset o (0..15) inside its 16-token group in the
+// head-dim-major copies (inverse of transpose.hip's order).
+__device__ __forceinline__ int pos16(int o) { return 8 * ((o >> 2) & 1) + 4 * (o >> 3) + (o & 3); }
+
+// LDS-DMA of 16 bytes per lane: lane l's data lands at lds_wave_base + 16 l.  Issued
+// as inline assembly so that the compiler does not guard every later LDS read
+// with a wait for it; completion is awaited explicitly (vmcnt) before the barrier
+// that publishes the tile.
+__device__ __forceinline__ void dma16(const void* g, const void* lds_wave_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(m0)) : "memory");
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// N MFMAs whose operand comes from LDS: PF reads stay in flight ahead of use, in
+// the order written (the compiler would otherwise pull each read next to its MFMA).
 template <int N, typename Load, typename Mma>
 __device__ __forceinline__ void pipelined(Load load, Mma mma) {
   bf16x8 ops[PF];
@@ -116,12 +116,12 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
   z[1] = f32x4{};
 }
 
-// ---- 2. main ----------------------------------------------------------------------
+// ---- 3. main ----------------------------------------------------------------------
 __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, int n_qtiles) {
-  __shared__ __attribute__((aligned(16))) bf16 Qs[2][BQ * HD];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[2][BQ * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Kst[BKV * HD];
-  __shared__ __attribute__((aligned(16))) bf16 dSt[BKV * BQ];
+  // per buffer: Q [64 rows][128], dO [64][128] (swz16), Q^T [128][64 positions],
+  // dO^T [128][64] (swz8) -- 4 tiles of 16 KB
+  __shared__ __attribute__((aligned(16))) bf16 stage[2][4 * TILE];
+  __shared__ __attribute__((aligned(16))) bf16 dSs[BQ * BKV];     // [row][key position]
   __shared__ __attribute__((aligned(16))) float lse2_s[2][BQ];
   __shared__ __attribute__((aligned(16))) float delta_s[2][BQ];
   __shared__ __attribute__((aligned(16))) int dsq_s[2][BQ];
@@ -131,7 +131,6 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, hi = lane >> 5;
-  const int g16 = lane >> 4, i16 = lane & 15;
   const int hk = blockIdx.x % f.Hkv;
   const int k0 = (int)(blockIdx.x / f.Hkv) * BKV;      // local first key of the block
   const int kw0 = k0 + wave * 32;                       // this wave's first key
@@ -150,6 +149,8 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   const bf16* __restrict__ kp = reinterpret_cast<const bf16*>(f.k);
   const bf16* __restrict__ vp = reinterpret_cast<const bf16*>(f.v);
   const bf16* __restrict__ dop = reinterpret_cast<const bf16*>(a.dout);
+  const bf16* __restrict__ qtp = reinterpret_cast<const bf16*>(a.qt);
+  const bf16* __restrict__ dotp = reinterpret_cast<const bf16*>(a.dot);
 
   // K and V fragments of this lane's key (B operands of S and dP): d = 16kk + 8hi + 0..7
   bf16x8 kf[8], vf[8];
@@ -162,48 +163,28 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
       vf[kk] = key_ok ? *reinterpret_cast<const bf16x8*>(vp + off + 16 * kk) : z;
     }
   }
-  // the block's K, row-major and swizzled in LDS, read once into the B operands of
-  // dQ = dS K: lane (d = 32*wave + r32, hi) holds K[16kc + 8(j/4) + 4hi + j%4][d]
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int c = tid + NWB * 64 * it;
-    const int key = c >> 4, lc = c & 15;
-    bf16x8 kv = {};
-    if (k0 + key < f.Sk)
-      kv = *reinterpret_cast<const bf16x8*>(kp + ((int64_t)(k0 + key) * f.Hkv + hk) * HD + lc * 8);
-    *reinterpret_cast<bf16x8*>(&Kst[key * HD + ((lc ^ swz16(key)) << 3)]) = kv;
-  }
-  __syncthreads();
-  // per-lane offsets of transposing reads from 128-wide rows: rows 16c + 4hi + i16/4 (+8),
-  // logical chunk 4*blk + 2(g16&1) + (i16&3)/2, half-chunk 4(i16&1)
-  auto tr16 = [&](int blk, int sec) {
-    const int row = 4 * hi + (i16 >> 2) + 8 * sec;
-    const int lc = 4 * blk + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-    return row * HD + ((lc ^ swz16(row)) << 3) + 4 * (i16 & 1);
-  };
+  // K operand of dQ = dS K: lane (d = 32*wave + r32, hi) holds K[key position
+  // 16kc + 8hi + j][d], from the head-dim-major copy (zero past Sk)
   bf16x8 kT[8];
+  {
+    const bf16* src = reinterpret_cast<const bf16*>(a.kt) +
+                      ((int64_t)hk * HD + 32 * wave + r32) * a.sk_pad + k0 + 8 * hi;
 #pragma unroll
-  for (int kc = 0; kc < 8; ++kc)
-    kT[kc] = tr_operand(&Kst[16 * kc * HD + tr16(wave, 0)], &Kst[16 * kc * HD + tr16(wave, 1)]);
-  int troff[4][2];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) { troff[db][0] = tr16(db, 0); troff[db][1] = tr16(db, 1); }
-  // 16-byte row reads of Q / dO (A operands of S, dP): row 32qb + r32, chunk 2kk + hi
+    for (int kc = 0; kc < 8; ++kc) kT[kc] = *reinterpret_cast<const bf16x8*>(src + 16 * kc);
+  }
+
+  // per-lane LDS offsets (elements), swizzled
+  //   Q / dO row reads (A operands of S, dP): row 32qb + r32, logical chunk 2kk + hi
+  //   Q^T / dO^T reads (A operands of dK, dV): row 32db + r32, logical chunk 2c + hi
+  //   dS reads (A operand of dQ): row 32qb + r32, logical chunk 2kc + hi
   int qoff[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) qoff[kk] = r32 * HD + (((2 * kk + hi) ^ swz16(r32)) << 3);
-  // dS^T [key][row]: transposing reads (A operand of dQ), rows 16kc + 4hi + i16/4 (+8)
-  int dsoff[2][2];
+  int toff[4];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int sec = 0; sec < 2; ++sec) {
-      const int row = 4 * hi + (i16 >> 2) + 8 * sec;
-      const int lc = 4 * qb + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-      dsoff[qb][sec] = row * BQ + ((lc ^ swz8(row)) << 3) + 4 * (i16 & 1);
-    }
-  const int dsrow = (wave * 32 + r32) * BQ;                // this lane's dS^T row (its key)
-  const int dsswz = swz8(wave * 32 + r32);
+  for (int c = 0; c < 4; ++c) toff[c] = r32 * BQ + (((2 * c + hi) ^ swz8(r32)) << 3);
+  // this lane's dS column: the key's position inside the block (16-token group order)
+  const int kpos = 32 * wave + 16 * (r32 >> 4) + pos16(r32 & 15);
 
   // ---- query tiles that can see the block: [t0, t1) ------------------------------
   int t0 = 0, t1 = n_qtiles;
@@ -221,29 +202,37 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   const int ntile = t1 - t0;
   const int n_items = ntile * grp;
 
-  // ---- staging of one (head, tile) item: 64 rows of Q and dO + per-row scalars ----
-  constexpr int CHUNKS = BQ * HD / 8 / (NWB * 64);   // 16-byte chunks per thread per tile
-  bf16x8 pq[CHUNKS], pd[CHUNKS];
-  float p_lse = 0.f, p_delta = 0.f;
-  int p_ds = 0, p_gq = 0;
-  auto load_item = [&](int it) {
+  // ---- staging of one (head, tile) item by LDS-DMA -----------------------------------
+  // Tile u (Q, dO, Q^T, dO^T) is 1024 16-byte chunks; wave w, instruction i covers
+  // flat physical chunks [(4i + w) * 64, +64), lane l the chunk (4i + w) * 64 + l.
+  auto dma_item = [&](int it, int buf) {
     const int h = hk * grp + it / ntile;
     const int q0 = (t0 + it % ntile) * BQ;
 #pragma unroll
-    for (int u = 0; u < CHUNKS; ++u) {
-      const int c = tid + NWB * 64 * u;
-      const int r = q0 + (c >> 4);
-      bf16x8 z = {};
-      pq[u] = z;
-      pd[u] = z;
-      if (r < f.Sq) {
-        const int64_t off = ((int64_t)r * f.Hq + h) * HD + (c & 15) * 8;
-        pq[u] = *reinterpret_cast<const bf16x8*>(qp + off);
-        pd[u] = *reinterpret_cast<const bf16x8*>(dop + off);
+    for (int i = 0; i < 4; ++i) {
+      const int blk = 4 * i + wave;
+      const int fc = blk * 64 + lane;
+      {   // Q, dO: row fc / 16 (clamped to a real row; the mask zeroes it), chunk fc % 16
+        const int row = fc >> 4, lc = (fc & 15) ^ swz16(row);
+        const int r = min(q0 + row, f.Sq - 1);
+        const int64_t off = ((int64_t)r * f.Hq + h) * HD + lc * 8;
+        dma16(qp + off, &stage[buf][0 * TILE + blk * 512]);
+        dma16(dop + off, &stage[buf][1 * TILE + blk * 512]);
+      }
+      {   // Q^T, dO^T: head-dim row fc / 8, positions q0 + 8 * chunk (padded copy)
+        const int row = fc >> 3, lc = (fc & 7) ^ swz8(row);
+        const int64_t off = ((int64_t)h * HD + row) * a.sq_pad + q0 + lc * 8;
+        dma16(qtp + off, &stage[buf][2 * TILE + blk * 512]);
+        dma16(dotp + off, &stage[buf][3 * TILE + blk * 512]);
       }
     }
+  };
+  float p_lse = 0.f, p_delta = 0.f;
+  int p_ds = 0, p_gq = 0;
+  auto load_scalars = [&](int it) {
     if (tid < BQ) {
-      const int r = q0 + tid;
+      const int h = hk * grp + it / ntile;
+      const int r = (t0 + it % ntile) * BQ + tid;
       const bool ok = r < f.Sq;
       const int g = f.q_start + r;
       p_lse = ok ? f.lse[(int64_t)h * f.lse_ld + r] * USP_LOG2E : 0.f;
@@ -252,20 +241,35 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
       p_gq = !ok ? -0x7fffffff : (f.causal ? g : 0x7fffffff);
     }
   };
-  auto store_item = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < CHUNKS; ++u) {
-      const int c = tid + NWB * 64 * u;
-      const int row = c >> 4, lc = c & 15;
-      const int off = row * HD + ((lc ^ swz16(row)) << 3);
-      *reinterpret_cast<bf16x8*>(&Qs[buf][off]) = pq[u];
-      *reinterpret_cast<bf16x8*>(&dOs[buf][off]) = pd[u];
-    }
+  auto store_scalars = [&](int buf) {
     if (tid < BQ) {
       lse2_s[buf][tid] = p_lse;
       delta_s[buf][tid] = p_delta;
       dsq_s[buf][tid] = p_ds;
       gq_s[buf][tid] = p_gq;
+    }
+  };
+  // dQ of an item: accumulated in registers, added to HBM one item later
+  f32x16 dqa[2];
+  int dq_h = 0, dq_q0 = 0;
+  bool dq_pending = false;
+  auto flush_dq = [&]() {
+    float* dqp = a.dq_acc + (int64_t)dq_h * HD + 32 * wave + r32;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if (dq_q0 + 32 * qb + 32 <= f.Sq) {   // wave-uniform: every row of the block exists
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = dq_q0 + 32 * qb + 8 * (i >> 2) + 4 * hi + (i & 3);
+          atomicAdd(dqp + (int64_t)q * f.Hq * HD, dqa[qb][i] * f.scale);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = dq_q0 + 32 * qb + 8 * (i >> 2) + 4 * hi + (i & 3);
+          if (q < f.Sq) atomicAdd(dqp + (int64_t)q * f.Hq * HD, dqa[qb][i] * f.scale);
+        }
+      }
     }
   };
 
@@ -274,17 +278,23 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   for (int i = 0; i < 4; ++i) { dka[i] = f32x16{}; dva[i] = f32x16{}; }
 
   if (n_items > 0) {
-    load_item(0);
-    store_item(0);
-    if (n_items > 1) load_item(1);
+    dma_item(0, 0);
+    load_scalars(0);
+    store_scalars(0);
+    if (n_items > 1) load_scalars(1);
+    wait_dma();
   }
   for (int it = 0; it < n_items; ++it) {
     const int buf = it & 1;
     const int h = hk * grp + it / ntile;
     const int q0 = (t0 + it % ntile) * BQ;
-    __syncthreads();   // item `it` staged; dS^T free
-    const bf16* Qb = Qs[buf];
-    const bf16* Db = dOs[buf];
+    __syncthreads();   // item `it` staged; dS free; buffer buf ^ 1 free
+    if (it + 1 < n_items) dma_item(it + 1, buf ^ 1);
+    if (dq_pending) flush_dq();
+    const bf16* Qb = &stage[buf][0 * TILE];
+    const bf16* Db = &stage[buf][1 * TILE];
+    const bf16* Qtb = &stage[buf][2 * TILE];
+    const bf16* Dtb = &stage[buf][3 * TILE];
 
     // fully visible (tile, wave keys) pairs skip the mask (wave-uniform)
     const int t_dsmax = __builtin_amdgcn_readfirstlane(wave_max(dsq_s[buf][lane]));
@@ -336,64 +346,54 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
           sb[i >> 3][i & 7] = (bf16)ds;
         }
       }
+      // ---- dS -> LDS [row][key position] ------------------------------------------------
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int q = 32 * qb + 8 * (i >> 2) + 4 * hi + (i & 3);
+        dSs[q * BKV + (((kpos >> 3) ^ swz16(q)) << 3) + (kpos & 7)] = sb[i >> 3][i & 7];
+      }
       __builtin_amdgcn_sched_barrier(0);
-      // ---- dV^T += dO^T P, dK^T += Q^T dS; k-slot j of half hi: row 16c+8(j/4)+4hi+j%4
-      // MFMA i: chunk cc = i / 8, head-dim block db = (i / 2) % 4, dV if i even else dK
+      // ---- dV^T += dO^T P, dK^T += Q^T dS -----------------------------------------------
+      // MFMA i: row chunk c = 2qb + i/8 (16 rows; k-slot j of lane half hi is row
+      // 16c + 8(j/4) + 4hi + j%4 = position 16c + 8hi + j), head-dim block db = (i/2)%4,
+      // dV if i is even else dK
       pipelined<16>(
           [&](int i) {
             const int c = 2 * qb + (i >> 3), db = (i >> 1) & 3;
-            const bf16* t = (i & 1) ? Qb : Db;
-            return tr_operand(&t[16 * c * HD + troff[db][0]], &t[16 * c * HD + troff[db][1]]);
+            const bf16* t = (i & 1) ? Qtb : Dtb;
+            return *reinterpret_cast<const bf16x8*>(&t[32 * db * BQ + toff[c]]);
           },
           [&](int i, const bf16x8& op) {
             const int cc = i >> 3, db = (i >> 1) & 3;
             if (i & 1) dka[db] = mfma32(op, sb[cc], dka[db]);
             else dva[db] = mfma32(op, pb[cc], dva[db]);
           });
-      // ---- dS^T -> LDS [key][row]: slots 4*half..+3 are rows 16c + 8*half + 4hi + 0..3
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int c = 2 * qb + cc;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const bf16x4 v4 = {sb[cc][4 * half], sb[cc][4 * half + 1], sb[cc][4 * half + 2],
-                             sb[cc][4 * half + 3]};
-          *reinterpret_cast<bf16x4*>(&dSt[dsrow + (((2 * c + half) ^ dsswz) << 3) + 4 * hi]) = v4;
-        }
-      }
     }
-    // ---- stage the next item into the other buffer; fetch the one after -------------
+    // ---- the next item's row scalars ---------------------------------------------------
     if (it + 1 < n_items) {
-      store_item(buf ^ 1);
-      if (it + 2 < n_items) load_item(it + 2);
+      store_scalars(buf ^ 1);
+      if (it + 2 < n_items) load_scalars(it + 2);
     }
-    __syncthreads();   // dS^T complete
+    __syncthreads();   // dS complete
 
-    // ---- dQ[rows][32 d of this wave] = dS K over the block's 128 keys -------------------
-    float* dqp = a.dq_acc + (int64_t)h * HD + 32 * wave + r32;
+    // ---- dQ[rows][32 d of this wave] = dS K over the block's 128 keys (MFMA kc: key
+    // positions 16kc + 8hi + 0..7 of lane half hi) --------------------------------------
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16 dqa = f32x16{};
+      dqa[qb] = f32x16{};
       pipelined<8>(
           [&](int kc) {
-            return tr_operand(&dSt[16 * kc * BQ + dsoff[qb][0]], &dSt[16 * kc * BQ + dsoff[qb][1]]);
+            return *reinterpret_cast<const bf16x8*>(
+                &dSs[(32 * qb + r32) * BKV + (((2 * kc + hi) ^ swz16(r32)) << 3)]);
           },
-          [&](int kc, const bf16x8& op) { dqa = mfma32(op, kT[kc], dqa); });
-      if (q0 + 32 * qb + 32 <= f.Sq) {   // wave-uniform: every row of the block exists
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = q0 + 32 * qb + 8 * (i >> 2) + 4 * hi + (i & 3);
-          atomicAdd(dqp + (int64_t)q * f.Hq * HD, dqa[i] * f.scale);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = q0 + 32 * qb + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if (q < f.Sq) atomicAdd(dqp + (int64_t)q * f.Hq * HD, dqa[i] * f.scale);
-        }
-      }
+          [&](int kc, const bf16x8& op) { dqa[qb] = mfma32(op, kT[kc], dqa[qb]); });
     }
+    dq_h = h;
+    dq_q0 = q0;
+    dq_pending = true;
+    wait_dma();   // item it+1 has landed (its DMA was issued a whole item ago)
   }
+  if (dq_pending) flush_dq();
 
   // ---- dK = scale dK^T, dV = dV^T (bf16), lane: key kl, d = 32db + 8g4 + 4hi + 0..3
   if (key_ok) {
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   }
 }
 
-// ---- 3. dQ accumulator -> bf16 -------------------------------------------------------
+// ---- 4. dQ accumulator -> bf16 -------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_bwd_post_kernel(const float* __restrict__ acc,
                                                             bf16* __restrict__ dq, int64_t n8) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -428,11 +428,33 @@ __global__ __launch_bounds__(256) void attn_bwd_post_kernel(const float* __restr
   reinterpret_cast<bf16x8*>(dq)[i] = o;
 }
 
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
 }  // namespace
 
-size_t attn_bwd_workspace_bytes(int64_t Sq, int32_t Hq, int32_t D) {
-  const size_t delta = ((size_t)Sq * Hq * sizeof(float) + 255) & ~(size_t)255;
-  return delta + (size_t)Sq * Hq * D * sizeof(float);
+size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D) {
+  const size_t sq_pad = (size_t)transpose_perm16_padded_len(Sq);
+  const size_t sk_pad = (size_t)transpose_perm16_padded_len(Sk);
+  return align256((size_t)Sq * Hq * sizeof(float))              // D
+         + align256((size_t)Sq * Hq * D * sizeof(float))        // dQ accumulator
+         + 2 * align256((size_t)Hq * D * sq_pad * sizeof(bf16))  // q^T, dout^T
+         + align256((size_t)Hkv * D * sk_pad * sizeof(bf16));    // k^T
+}
+
+void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
+  const AttnArgs& f = a.f;
+  a.sq_pad = transpose_perm16_padded_len(f.Sq);
+  a.sk_pad = transpose_perm16_padded_len(f.Sk);
+  char* p = reinterpret_cast<char*>(base);
+  a.delta = reinterpret_cast<float*>(p);
+  p += align256((size_t)f.Sq * f.Hq * sizeof(float));
+  a.dq_acc = reinterpret_cast<float*>(p);
+  p += align256((size_t)f.Sq * f.Hq * HD * sizeof(float));
+  a.qt = p;
+  p += align256((size_t)f.Hq * HD * a.sq_pad * sizeof(bf16));
+  a.dot = p;
+  p += align256((size_t)f.Hq * HD * a.sq_pad * sizeof(bf16));
+  a.kt = p;
 }
 
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
@@ -441,8 +463,13 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   if (rows > 0) {
     hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0,
                        stream, a);
+    hipError_t e = launch_transpose_perm16(f.q, f.Sq, f.Hq, a.qt, stream);
+    if (e == hipSuccess) e = launch_transpose_perm16(a.dout, f.Sq, f.Hq, a.dot, stream);
+    if (e != hipSuccess) return e;
   }
   if (f.Sk > 0) {
+    hipError_t e = launch_transpose_perm16(f.k, f.Sk, f.Hkv, a.kt, stream);
+    if (e != hipSuccess) return e;
     const int n_ktiles = (f.Sk + BKV - 1) / BKV;
     const int n_qtiles = (f.Sq + BQ - 1) / BQ;
     hipLaunchKernelGGL(attn_bwd_main_kernel, dim3((unsigned)(n_ktiles * f.Hkv)), dim3(NWB * 64), 0,

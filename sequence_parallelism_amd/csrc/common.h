@@ -56,10 +56,17 @@ struct AttnBwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;        // workspace: [Hq][Sq]
-  float* dq_acc;       // workspace: [Sq][Hq][D] fp32
+  // workspace regions
+  float* delta;        // [Hq][Sq] fp32
+  float* dq_acc;       // [Sq][Hq][D] fp32
+  void* qt;            // [Hq][D][sq_pad] bf16, head-dim-major q (transpose.hip order)
+  void* dot;           // [Hq][D][sq_pad] bf16, head-dim-major dout
+  void* kt;            // [Hkv][D][sk_pad] bf16, head-dim-major k
+  int64_t sq_pad, sk_pad;
 };
-size_t attn_bwd_workspace_bytes(int64_t Sq, int32_t Hq, int32_t D);
+size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D);
+// fills the workspace pointers of a from its base (layout of attn_bwd_workspace_bytes)
+void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base);
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s);
 
 // Y[h][d][p] = X[tok(p)][h][d] over a padded token axis, 16-token groups permuted

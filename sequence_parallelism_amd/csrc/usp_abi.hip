@@ -137,10 +137,11 @@ usp_status blockattn_fwd(const void* q, const void* k, const void* v, int64_t Sq
   return hip_status(launch_attn_fwd_f32(a, s));
 }
 
-usp_status blockattn_bwd_workspace_size(int64_t Sq, int32_t Hq, int32_t D, size_t* bytes) {
+usp_status blockattn_bwd_workspace_size(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D,
+                                        size_t* bytes) {
   if (!bytes) return USP_ERR_NULL_POINTER;
-  if (Sq < 0 || Hq < 1 || D < 1) return USP_ERR_BAD_SHAPE;
-  *bytes = attn_bwd_workspace_bytes(Sq, Hq, D);
+  if (Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1) return USP_ERR_BAD_SHAPE;
+  *bytes = attn_bwd_workspace_bytes(Sq, Sk, Hq, Hkv, D);
   return USP_OK;
 }
 
@@ -155,12 +156,12 @@ usp_status blockattn_bwd(const void* q, const void* k, const void* v, const void
   if (st != USP_OK) return st;
   if (Sq > 0 && (!dout || !dq)) return USP_ERR_NULL_POINTER;
   if (Sk > 0 && (!dk || !dv)) return USP_ERR_NULL_POINTER;
-  if (!workspace && attn_bwd_workspace_bytes(Sq, Hq, D) > 0) return USP_ERR_NULL_POINTER;
+  if (!workspace && attn_bwd_workspace_bytes(Sq, Sk, Hq, Hkv, D) > 0) return USP_ERR_NULL_POINTER;
   if (in_dtype != USP_BF16) return USP_ERR_UNSUPPORTED;
   if (!(aligned(dout, 16) && aligned(dq, 16) && aligned(dk, 8) && aligned(dv, 8) &&
         aligned(workspace, 256)))
     return USP_ERR_MISALIGNED;
-  const size_t need = attn_bwd_workspace_bytes(Sq, Hq, D);
+  const size_t need = attn_bwd_workspace_bytes(Sq, Sk, Hq, Hkv, D);
   if (workspace_bytes < need) return USP_ERR_WORKSPACE_TOO_SMALL;
   AttnBwdArgs a;
   a.f = make_args(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal, softmax_scale,
@@ -169,9 +170,7 @@ usp_status blockattn_bwd(const void* q, const void* k, const void* v, const void
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.delta = reinterpret_cast<float*>(workspace);
-  a.dq_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                      (((size_t)Sq * Hq * sizeof(float) + 255) & ~(size_t)255));
+  attn_bwd_workspace_layout(a, workspace);
   return hip_status(launch_attn_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -101,10 +101,10 @@ def test_fwd_validation(lib):
 
 def test_bwd_validation(lib):
     n = ctypes.c_size_t(0)
-    assert lib.blockattn_bwd_workspace_size(256, 4, 128, ctypes.byref(n)) == OK
+    assert lib.blockattn_bwd_workspace_size(256, 256, 4, 1, 128, ctypes.byref(n)) == OK
     assert n.value >= 256 * 4 * 128 * 4 + 256 * 4 * 4
-    assert lib.blockattn_bwd_workspace_size(256, 4, 128, None) == NULLP
-    assert lib.blockattn_bwd_workspace_size(-1, 4, 128, ctypes.byref(n)) == SHAPE
+    assert lib.blockattn_bwd_workspace_size(256, 256, 4, 1, 128, None) == NULLP
+    assert lib.blockattn_bwd_workspace_size(-1, 256, 4, 1, 128, ctypes.byref(n)) == SHAPE
 
     def bwd(ws_bytes=n.value, ws=A, dq=A, dt=0, Hq=4, Hkv=1, D=128):
         return lib.blockattn_bwd(A, A, A, A, A, 256, A, 256, 256, Hq, Hkv, D, A, 0, 0, 1, 0.1, dt,
