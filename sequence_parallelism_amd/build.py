@@ -12,13 +12,14 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libusp.so")
-SOURCES = ["usp_abi.hip", "permute.hip", "merge.hip", "transpose.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["usp_abi.hip", "permute.hip", "merge.hip", "transpose.hip", "attn_fwd.hip", "attn_bwd.hip",
+           "attn_bwd_dq.hip"]
 
-# gfx950 only; packed-FP32 VALU instructions disabled; hardware fp32 atomics.
+# gfx950 only; packed-FP32 VALU instructions disabled.
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics", "-Wno-unused-command-line-argument",
+    "-Wno-unused-command-line-argument",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

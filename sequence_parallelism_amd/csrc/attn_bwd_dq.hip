@@ -1,0 +1,248 @@
+// dQ of the blockwise attention share (gfx950, bf16, head dim 128): the query-
+// stationary half of the backward.  With P = exp(scale q k^T + mask - lse) and
+// D_i = <dO_i, O_i> (both as in attn_bwd.hip),
+//   dQ = scale dS K,   dS = P * (dO V^T - D),
+// so a workgroup that owns a block of query rows recomputes S and dP for every key
+// tile it can see and accumulates dQ in registers: no atomics and no fp32
+// accumulator in memory (an fp32 atomic per (row, key block) runs into the L2
+// atomic rate, about 1.3 TB/s on MI355X, long before the MFMAs are busy).
+//
+//   * a workgroup is 8 wavefronts (2 per SIMD) and owns 256 query rows of one head;
+//     each wave owns 32 rows with their Q and dO fragments in registers;
+//   * key tiles of 64 keys are staged in double-buffered LDS by LDS-DMA one tile
+//     ahead: K and V row-major, and K^T from the head-dim-major copy made for the
+//     dK/dV kernel (token order inside each 16-token group = the lanes' score
+//     slots), so every MFMA operand read from LDS is one 16-byte read;
+//   * S^T = K Q^T and dP^T = V dO^T come out with one query per lane (32 MFMAs,
+//     two interleaved accumulator chains each); P and dS are formed in registers and
+//     dS^T (bf16) feeds dQ^T += K^T dS^T directly (16 MFMAs);
+//   * tiles fully visible to a wave skip the per-element mask.
+#include "gfx950.h"
+
+namespace {
+
+using namespace gfx950;
+
+constexpr int HD = 128;          // head dim
+constexpr int NW = 8;            // wavefronts per workgroup
+constexpr int BR = 32 * NW;      // query rows per workgroup
+constexpr int BC = 64;           // keys per LDS tile
+constexpr int PF = 4;            // LDS operand reads in flight ahead of their MFMA
+constexpr int TILE = BC * HD;    // elements of one staged tile (16 KB)
+constexpr int NXCD = 8;          // MI355X dispatches workgroup i to XCD i % 8
+static_assert(TILE / 8 == 2 * NW * 64, "a staged tile is two 64-lane DMA loads per wave");
+
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int n_qtiles) {
+  // per buffer: K [64 keys][128], V [64 keys][128] (swz16), K^T [128][64 positions] (swz8)
+  __shared__ __attribute__((aligned(16))) bf16 stage[2][3 * TILE];
+  __shared__ int red[NW][2];
+
+  const AttnArgs& f = a.f;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, hi = lane >> 5;
+  // XCD-aware order (as in the forward): the workgroups an XCD runs back to back are
+  // the query heads of one query tile, tiles taken every NXCD-th from the longest
+  // causal rows down
+  const int xcd = blockIdx.x % NXCD, j = blockIdx.x / NXCD;
+  const int h = j % f.Hq;
+  const int qt = n_qtiles - 1 - ((j / f.Hq) * NXCD + xcd);
+  if (qt < 0) return;                                       // grid padding (whole workgroup)
+  const int hk = h / (f.Hq / f.Hkv);
+  const int row = qt * BR + wave * 32 + r32;
+  const bool row_ok = row < f.Sq;
+  const int gq = f.q_start + row;
+
+  // ---- visible key ranges (global token indices) --------------------------------
+  int ds = 0x7fffffff;
+  int lo = 0x7fffffff, hiex = -0x7fffffff, ds_max = -0x7fffffff, gq_min = 0x7fffffff;
+  if (row_ok) {
+    ds = f.causal ? gq - f.pos[gq] : f.k_start;
+    lo = ds;
+    hiex = f.causal ? gq + 1 : f.k_start + f.Sk;
+    ds_max = ds;
+    gq_min = gq;
+  }
+  const int w_lo = __builtin_amdgcn_readfirstlane(wave_min(lo));
+  const int w_hiex = __builtin_amdgcn_readfirstlane(wave_max(hiex));
+  const int w_dsmax = __builtin_amdgcn_readfirstlane(wave_max(ds_max));
+  const int w_gqmin = __builtin_amdgcn_readfirstlane(wave_min(gq_min));
+  if (lane == 0) { red[wave][0] = w_lo; red[wave][1] = w_hiex; }
+  __syncthreads();
+  int g_lo = red[0][0], g_hiex = red[0][1];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) { g_lo = min(g_lo, red[w][0]); g_hiex = max(g_hiex, red[w][1]); }
+  g_lo = __builtin_amdgcn_readfirstlane(g_lo);
+  g_hiex = __builtin_amdgcn_readfirstlane(g_hiex);
+  // local key range [kb, ke); tiles start on 16-key groups (the K^T slot order)
+  const int ke = min(g_hiex, f.k_start + f.Sk) - f.k_start;
+  const int kb = (max(g_lo, f.k_start) - f.k_start) & ~15;
+
+  // ---- Q and dO fragments (B operands of S^T = K Q^T, dP^T = V dO^T):
+  // row r32, d = 16 kk + 8 hi + 0..7 ------------------------------------------------
+  bf16x8 qf[8], df[8];
+  {
+    const int64_t off = ((int64_t)(row_ok ? row : 0) * f.Hq + h) * HD + 8 * hi;
+    const bf16* qsrc = reinterpret_cast<const bf16*>(f.q) + off;
+    const bf16* dsrc = reinterpret_cast<const bf16*>(a.dout) + off;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      bf16x8 z = {};
+      qf[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(qsrc + 16 * kk) : z;
+      df[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(dsrc + 16 * kk) : z;
+    }
+  }
+  // row scalars: lse in log2 units (+inf for a row with no visible key, so that P = 0
+  // there) and D
+  float lse2 = INFINITY, dlt = 0.f;
+  if (row_ok) {
+    const float l = f.lse[(int64_t)h * f.lse_ld + row];
+    lse2 = l == -INFINITY ? INFINITY : l * USP_LOG2E;
+    dlt = a.delta[(int64_t)h * f.Sq + row];
+  }
+  const float sl2 = f.scale * USP_LOG2E;
+
+  // ---- staging by LDS-DMA: tile u (K, V, K^T), load i (0..1) of wave w covers
+  // physical chunks [(8i + w) * 64, +64), lane l the chunk (8i + w) * 64 + l:
+  //   K, V: key row 32i + 4w + l/16, physical chunk l%16;
+  //   K^T:  head-dim row 64i + 8w + l/8, physical chunk l%8.
+  // The swizzle depends on the row modulo 16 only, so one lane offset serves both loads.
+  const uint32_t kr0 = (uint32_t)(4 * wave + (lane >> 4));
+  const uint32_t k_lc = (uint32_t)((((lane & 15) ^ swz16(kr0)) << 3) * 2);
+  const uint32_t rowkB = (uint32_t)f.Hkv * HD * 2;                // bytes per k / v row
+  const int td0 = 8 * wave + (lane >> 3);
+  const uint32_t t_off = (uint32_t)((td0 * a.sk_pad + (((lane & 7) ^ swz8(td0)) << 3)) * 2);
+  const uint32_t stage_lds = lds_addr(&stage[0][0]);
+  auto dma_step = [&](int s, int kt, int buf) {   // s = 2u + i
+    const int u = s >> 1, i = s & 1;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        stage_lds + (uint32_t)(((buf * 3 + u) * TILE + (NW * i + wave) * 512) * 2));
+    if (u < 2) {   // keys past Sk are clamped to the last key (the mask zeroes them)
+      const uint32_t lim = (uint32_t)(f.Sk - 1 - kt);
+      const uint32_t voff = min(kr0 + 32 * i, lim) * rowkB + k_lc;
+      const char* base = reinterpret_cast<const char*>(u == 0 ? f.k : f.v) +
+                         ((int64_t)kt * f.Hkv + hk) * HD * 2;
+      dma16(base, voff, lds);
+    } else {
+      const char* base = reinterpret_cast<const char*>(a.kt) +
+                         (((int64_t)hk * HD + 64 * i) * a.sk_pad + kt) * 2;
+      dma16(base, t_off, lds);
+    }
+  };
+
+  // per-lane element offsets inside the tiles: chunk 2k + hi of row r sits at
+  // (2k + hi) ^ swz(r), i.e. at  base ^ 16k  with base = r * len + 8 (hi ^ swz(r))
+  //   K, V (A operands of S^T, dP^T): row 32 kb2 + r32, chunks 2 kk + hi
+  //   K^T (A operand of dQ^T): head-dim row 32 db + r32, chunks 2c + hi (positions
+  //   16c + 8hi .. +7 = the lane half's eight key slots of chunk c)
+  const int kbase = r32 * HD + ((hi ^ swz16(r32)) << 3);
+  const int tbase = r32 * BC + ((hi ^ swz8(r32)) << 3);
+
+  f32x16 dqacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dqacc[i] = f32x16{};
+
+  if (kb < ke) {
+    for (int s = 0; s < 6; ++s) dma_step(s, kb, 0);
+    wait_vmem();
+    __syncthreads();
+  }
+  const int last_kt = kb + ((ke - kb - 1) / BC) * BC;
+  int buf = 0;
+  for (int kt = kb; kt < ke; kt += BC, buf ^= 1) {
+    const bf16* Kb = &stage[buf][0];
+    const bf16* Vb = &stage[buf][TILE];
+    const bf16* Tb = &stage[buf][2 * TILE];
+    const int ktn = min(kt + BC, last_kt);   // the last tile fetches itself again (unused)
+
+    // ---- S^T and dP^T: 64 keys x 32 queries each.  MFMA i: S (even i) or dP (odd i)
+    // of key block kb2 = (i/2)%2, d chunk kk = i/4; the next tile's DMA rides along --
+    f32x16 sacc[2], dpacc[2];
+    mfma_pipeline<PF, 32>(
+        [&](auto I) {
+          constexpr int i = decltype(I)::v, kb2 = (i >> 1) & 1, kk = i >> 2;
+          const bf16* t = (i & 1) ? Vb : Kb;
+          return *reinterpret_cast<const bf16x8*>(&t[32 * kb2 * HD + (kbase ^ (16 * kk))]);
+        },
+        [&](auto I, const bf16x8& op) {
+          constexpr int i = decltype(I)::v, kb2 = (i >> 1) & 1, kk = i >> 2;
+          if constexpr (i & 1) dpacc[kb2] = mfma32(op, df[kk], kk == 0 ? f32x16{} : dpacc[kb2]);
+          else sacc[kb2] = mfma32(op, qf[kk], kk == 0 ? f32x16{} : sacc[kb2]);
+        },
+        [&](auto I) {
+          constexpr int i = decltype(I)::v;
+          if constexpr (i % 4 == 1 && i / 4 < 6) dma_step(i / 4, ktn, buf ^ 1);
+        });
+
+    // ---- mask (boundary tiles only; wave-uniform branch) ---------------------------
+    const int gk0 = f.k_start + kt;
+    const bool full = (kt + BC <= ke) && (!f.causal || (gk0 + BC - 1 <= w_gqmin && gk0 >= w_dsmax));
+    if (!full) {
+      const int klim = ke - kt;
+      // visible: lo_k <= key <= hi_k (no int32 overflow: ds, gq, gk0 are in [0, 2^31))
+      const int lo_k = f.causal ? max(ds - gk0, kb - kt) : kb - kt;
+      const int hi_k = f.causal ? gq - gk0 : BC;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = 32 * kb2 + 8 * (i >> 2) + 4 * hi + (i & 3);
+          const bool vis = (key < klim) & (key >= lo_k) & (key <= hi_k);
+          sacc[kb2][i] = vis ? sacc[kb2][i] : -INFINITY;
+        }
+      }
+    }
+    // ---- P = 2^(s sl2 - lse2), dS = P (dP - D), as bf16 B operands: chunk c = 2 kb2
+    // + half holds elements 8 half + 0..7 of key block kb2 ------------------------------
+    bf16x8 sb[4];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][e], sl2, -lse2));
+        sb[2 * kb2 + (e >> 3)][e & 7] = (bf16)(p * (dpacc[kb2][e] - dlt));
+      }
+    }
+    // ---- dQ^T += K^T dS^T (MFMA i: key chunk c = i/4, head-dim block db = i%4) --------
+    mfma_pipeline<PF, 16>(
+        [&](auto I) {
+          constexpr int i = decltype(I)::v, c = i >> 2, db = i & 3;
+          return *reinterpret_cast<const bf16x8*>(&Tb[32 * db * BC + (tbase ^ (16 * c))]);
+        },
+        [&](auto I, const bf16x8& op) {
+          constexpr int i = decltype(I)::v, c = i >> 2, db = i & 3;
+          dqacc[db] = mfma32(op, sb[c], dqacc[db]);
+        },
+        [&](auto) {});
+    wait_vmem();       // the next tile has landed in the other buffer
+    __syncthreads();   // ... for every wave; this buffer is free again
+  }
+
+  // ---- epilogue: dQ = scale dQ^T (bf16); lane: row r32, d = 32 db + 8 g4 + 4 hi + 0..3
+  if (row_ok) {
+    bf16* dqp = reinterpret_cast<bf16*>(a.dq) + ((int64_t)row * f.Hq + h) * HD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * db + 8 * g4 + 4 * hi;
+        const bf16x4 v = {(bf16)(dqacc[db][4 * g4] * f.scale), (bf16)(dqacc[db][4 * g4 + 1] * f.scale),
+                          (bf16)(dqacc[db][4 * g4 + 2] * f.scale), (bf16)(dqacc[db][4 * g4 + 3] * f.scale)};
+        *reinterpret_cast<bf16x4*>(dqp + d) = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// a must carry the workspace regions of attn_bwd_workspace_layout, with D and the
+// head-dim-major k already written (launch_attn_bwd_bf16 does both first).
+hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, hipStream_t stream) {
+  const AttnArgs& f = a.f;
+  if (f.Sq == 0) return hipSuccess;
+  const int n_qtiles = (f.Sq + BR - 1) / BR;
+  dim3 grid((unsigned)(((n_qtiles + NXCD - 1) / NXCD) * NXCD * f.Hq));
+  hipLaunchKernelGGL(attn_bwd_dq_kernel, grid, dim3(NW * 64), 0, stream, a, n_qtiles);
+  return hipGetLastError();
+}

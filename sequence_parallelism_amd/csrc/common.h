@@ -58,7 +58,6 @@ struct AttnBwdArgs {
   void* dv;
   // workspace regions
   float* delta;        // [Hq][Sq] fp32
-  float* dq_acc;       // [Sq][Hq][D] fp32
   void* qt;            // [Hq][D][sq_pad] bf16, head-dim-major q (transpose.hip order)
   void* dot;           // [Hq][D][sq_pad] bf16, head-dim-major dout
   void* kt;            // [Hkv][D][sk_pad] bf16, head-dim-major k
@@ -67,7 +66,11 @@ struct AttnBwdArgs {
 size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D);
 // fills the workspace pointers of a from its base (layout of attn_bwd_workspace_bytes)
 void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base);
+// false when an offset the backward keeps in 32 bits would not fit
+bool attn_bwd_supported(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv);
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s);
+// the query-stationary dQ kernel (attn_bwd_dq.hip), launched by launch_attn_bwd_bf16
+hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, hipStream_t s);
 
 // Y[h][d][p] = X[tok(p)][h][d] over a padded token axis, 16-token groups permuted
 // to MFMA slot order (transpose.hip); D = 128, bf16.

@@ -1,0 +1,77 @@
+// Device helpers shared by the attention kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <utility>
+
+#include "common.h"
+
+namespace gfx950 {
+
+// D = A B + C with A 32x16, B 16x32 (bf16), C/D 32x32 fp32.  Lane l holds A row l%32
+// (B column l%32), reduction slots 8(l/32) + 0..7; accumulator register i of lane l is
+// row 8(i/4) + 4(l/32) + i%4, column l%32.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS tiles are unpadded; 16-byte chunk c of row r is stored at c ^ swz(r).  With
+// these, 16 lanes reading 16 consecutive rows at one logical chunk touch all 64
+// banks once.  Rows of 128 bf16 have 16 chunks, rows of 64 bf16 have 8.
+__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
+// Compile-time loop: f(IC<0>{}), f(IC<1>{}), ..., so every index is a constant.
+template <int N> struct IC { static constexpr int v = N; };
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(F& f, std::integer_sequence<int, I...>) {
+  (f(IC<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// NS MFMAs whose A operand comes from LDS: the read for MFMA i is issued PF steps
+// ahead; side(i) is issued right after MFMA i, so its VALU / LDS / memory work runs
+// while the matrix core executes.  A scheduling fence keeps every step in place (the
+// compiler would otherwise pull each read next to its MFMA and bunch the side work).
+template <int PF, int NS, typename Load, typename Mma, typename Side>
+__device__ __forceinline__ void mfma_pipeline(Load&& load, Mma&& mma, Side&& side) {
+  bf16x8 ops[PF];
+  unroll<(PF < NS ? PF : NS)>([&](auto I) { ops[decltype(I)::v] = load(I); });
+  unroll<NS>([&](auto I) {
+    constexpr int i = decltype(I)::v;
+    const bf16x8 op = ops[i % PF];
+    if constexpr (i + PF < NS) ops[i % PF] = load(IC<i + PF>{});
+    mma(I, op);
+    side(I);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// LDS-DMA of 16 bytes per lane from sbase + voff (sbase wave-uniform): lane l's data
+// lands at LDS byte address lds + 16 l.  Issued as inline assembly so that the
+// compiler does not guard every later LDS read with a wait for it; completion is
+// awaited explicitly (wait_vmem) before the barrier that publishes the tile.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+__device__ __forceinline__ int wave_min(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = min(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off));
+  return x;
+}
+
+}  // namespace gfx950

@@ -158,6 +158,7 @@ usp_status blockattn_bwd(const void* q, const void* k, const void* v, const void
   if (Sk > 0 && (!dk || !dv)) return USP_ERR_NULL_POINTER;
   if (!workspace && attn_bwd_workspace_bytes(Sq, Sk, Hq, Hkv, D) > 0) return USP_ERR_NULL_POINTER;
   if (in_dtype != USP_BF16) return USP_ERR_UNSUPPORTED;
+  if (!attn_bwd_supported(Sq, Sk, Hq, Hkv)) return USP_ERR_UNSUPPORTED;
   if (!(aligned(dout, 16) && aligned(dq, 16) && aligned(dk, 8) && aligned(dv, 8) &&
         aligned(workspace, 256)))
     return USP_ERR_MISALIGNED;
