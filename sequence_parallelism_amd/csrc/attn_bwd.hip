@@ -22,8 +22,9 @@
 //                   S, dP of rows 0-31 | S, dP of rows 32-63 | dV^T, dK^T of rows
 //                   0-31 | dV^T, dK^T of rows 32-63,
 //                 and after every MFMA it issues one piece of independent work that
-//                 the matrix core's execution hides: the next item's DMA, then P and
-//                 dS of the previous 32 rows (exp2, products, bf16 packing);
+//                 the matrix core's execution hides: the next item's DMA (spread over
+//                 the whole item), and P and dS of the previous 32 rows (exp2,
+//                 products, bf16 packing);
 //   4. dQ:        attn_bwd_dq.hip, query-stationary, recomputing S and dP (no atomics).
 // Query tiles that cannot see the key block are not visited (the first visible
 // tile follows from the block's first key, the last from a binary search over
@@ -43,7 +44,7 @@ constexpr int BQ = 64;              // query rows per item
 constexpr int PF = 4;               // LDS operand reads in flight ahead of their MFMA
 constexpr int TILE = BQ * HD;       // elements of one staged tile (16 KB)
 static_assert(TILE / 8 == 4 * NWB * 64, "a staged tile is four 64-lane DMA loads per wave");
-static_assert(BQ <= NWB * 64, "one thread per query row stages the row scalars");
+static_assert(BQ == 64, "one lane per query row stages the row scalars");
 
 // ---- 1. D = rowsum(dO * O) -------------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
@@ -183,26 +184,29 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
     }
   };
 
-  // row scalars of an item, staged by the first BQ threads one item ahead
+  // Row scalars of an item, one row per lane, read one item ahead.  The reads are
+  // issued by every wave with no arithmetic on their results (that would stall the
+  // pipeline they sit in for a whole memory latency); wave 0 finishes and stores
+  // them at the end of the item.
   float p_lse = 0.f, p_delta = 0.f;
-  int p_ds = 0, p_gq = 0;
+  int p_pos = 0, p_q0 = 0;
+  const int* const pos_or_dummy = f.causal ? f.pos : reinterpret_cast<const int*>(f.lse);
   auto load_scalars = [&](int h, int q0) {
-    if (tid < BQ) {
-      const int r = q0 + tid;
-      const bool ok = r < f.Sq;
-      const int g = f.q_start + r;
-      p_lse = ok ? f.lse[(int64_t)h * f.lse_ld + r] * USP_LOG2E : 0.f;
-      p_delta = ok ? a.delta[(int64_t)h * f.Sq + r] : 0.f;
-      p_ds = !ok ? 0x7fffffff : (f.causal ? g - f.pos[g] : -0x7fffffff);
-      p_gq = !ok ? -0x7fffffff : (f.causal ? g : 0x7fffffff);
-    }
+    const int r = min(q0 + lane, f.Sq - 1);
+    p_lse = f.lse[(int64_t)h * f.lse_ld + r];
+    p_delta = a.delta[(int64_t)h * f.Sq + r];
+    p_pos = pos_or_dummy[f.causal ? f.q_start + r : 0];
+    p_q0 = q0;
   };
   auto store_scalars = [&](int buf) {
-    if (tid < BQ) {
-      lse2_s[buf][tid] = p_lse;
-      delta_s[buf][tid] = p_delta;
-      dsq_s[buf][tid] = p_ds;
-      gq_s[buf][tid] = p_gq;
+    if (wave == 0) {
+      const int r = p_q0 + lane;
+      const bool ok = r < f.Sq;
+      const int g = f.q_start + r;
+      lse2_s[buf][lane] = ok ? p_lse * USP_LOG2E : 0.f;
+      delta_s[buf][lane] = ok ? p_delta : 0.f;
+      dsq_s[buf][lane] = !ok ? 0x7fffffff : (f.causal ? g - p_pos : -0x7fffffff);
+      gq_s[buf][lane] = !ok ? -0x7fffffff : (f.causal ? g : 0x7fffffff);
     }
   };
 
@@ -252,22 +256,27 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
       f32x16 sacc[2], dpacc[2];
       f32x4 l4[2][4], e4[2][4];
       bf16x8 pb[2][2], sb[2][2];
-      float p_prev = 0.f, s_prev = 0.f;
       uint32_t vq = 0;
 
-      // P and dS of element e of 32-row block qb (row 32qb + 8(e/4) + 4hi + e%4)
-      auto softmax = [&](auto QB, auto E) {
+      // P and dS of element e of 32-row block qb (row 32qb + 8(e/4) + 4hi + e%4), in two
+      // stages one step apart so that no instruction waits on the exponential:
+      //   A: P = 2^(s sl2 - lse2);   B: dS = P (dP - D), and P, dS packed to bf16 pairs
+      float pv[2][16];
+      float ds_prev = 0.f;
+      auto soft_a = [&](auto QB, auto E) {
         constexpr int qb = decltype(QB)::v, e = decltype(E)::v;
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][e], sl2, -l4[qb][e >> 2][e & 3]));
-        const float ds = p * (dpacc[qb][e] - e4[qb][e >> 2][e & 3]);
+        pv[qb][e] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][e], sl2, -l4[qb][e >> 2][e & 3]));
+      };
+      auto soft_b = [&](auto QB, auto E) {
+        constexpr int qb = decltype(QB)::v, e = decltype(E)::v;
+        const float ds = pv[qb][e] * (dpacc[qb][e] - e4[qb][e >> 2][e & 3]);
         if constexpr (e & 1) {
-          pb[qb][e >> 3][(e & 7) - 1] = (bf16)p_prev;
-          pb[qb][e >> 3][e & 7] = (bf16)p;
-          sb[qb][e >> 3][(e & 7) - 1] = (bf16)s_prev;
+          pb[qb][e >> 3][(e & 7) - 1] = (bf16)pv[qb][e - 1];
+          pb[qb][e >> 3][e & 7] = (bf16)pv[qb][e];
+          sb[qb][e >> 3][(e & 7) - 1] = (bf16)ds_prev;
           sb[qb][e >> 3][e & 7] = (bf16)ds;
         } else {
-          p_prev = p;
-          s_prev = ds;
+          ds_prev = ds;
         }
       };
       // row scalars of rows 32qb + 8g4 + 4hi + 0..3, read four steps before first use
@@ -321,13 +330,18 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
               constexpr int qb = i < 28 ? 0 : 1, g4 = (i - 12 - 16 * qb) / 4;
               load_rows(IC<qb>{}, IC<g4>{});
             }
-            if constexpr (slot == 0) {
-              if constexpr (j == 1) load_scalars(hn, q0n);   // item it+1's row scalars
-              dma_step(j, hn, q0n, buf ^ 1, vq);
-            } else if constexpr (slot == 1) {
-              softmax(IC<0>{}, IC<j>{});
+            if constexpr (i % 4 == 1) dma_step(i / 4, hn, q0n, buf ^ 1, vq);   // item it+1
+            if constexpr (i == 2) load_scalars(hn, q0n);                           // its row scalars
+            // block 0's softmax behind block 1's S, dP; block 1's behind block 0's dV, dK
+            if constexpr (slot == 1) {
+              soft_a(IC<0>{}, IC<j>{});
+              if constexpr (j >= 1) soft_b(IC<0>{}, IC<j - 1>{});
             } else if constexpr (slot == 2) {
-              softmax(IC<1>{}, IC<j>{});
+              if constexpr (j == 0) soft_b(IC<0>{}, IC<15>{});
+              soft_a(IC<1>{}, IC<j>{});
+              if constexpr (j >= 1) soft_b(IC<1>{}, IC<j - 1>{});
+            } else if constexpr (slot == 3) {
+              if constexpr (j == 0) soft_b(IC<1>{}, IC<15>{});
             }
           });
     }
