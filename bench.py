@@ -94,7 +94,7 @@ def main():
     o_seq, dxq = torch.zeros_like(xq), torch.zeros_like(xq)
     dxk, dxv = torch.zeros_like(xk), torch.zeros_like(xv)
     ws = torch.empty(usp.bwd_workspace_bytes(S, S, hq, hkv, D), dtype=torch.uint8, device=dev)
-    ws_f = torch.empty(usp.fwd_workspace_bytes(S, hkv, D), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(usp.fwd_workspace_bytes(S, S, hq, hkv, D), dtype=torch.uint8, device=dev)
 
     vis = int(np.sum(lengths * (lengths + 1) // 2))
     fwd_flop = 4.0 * D * vis * hq

@@ -120,8 +120,8 @@ usp_status usp_head_to_seq_permute(void* dst, const void* src, int32_t P, int64_
  * Supported: in_dtype BF16 with D = 128 (MFMA path; o_dtype BF16 or F32);
  *            in_dtype F32 with 1 <= D <= 128 (o_dtype F32).
  * workspace: caller-owned device buffer of at least blockattn_fwd_workspace_size()
- *   bytes, 16-byte aligned (the bf16 path keeps a head-dim-major copy of v there;
- *   the f32 path needs none and accepts NULL).  Its contents on entry do not
+ *   bytes, 16-byte aligned (the bf16 path keeps a head-dim-major copy of v and the
+ *   launch order of the query tiles there; the f32 path needs none and accepts NULL).  Its contents on entry do not
  *   matter and are clobbered; it must not overlap any other argument.
  * Alignment: bf16 q, k, v, o 16-byte aligned.
  * Errors: NULL pointers (position_ids only when causal); Sq, Sk < 0; Hq, Hkv < 1;
@@ -137,8 +137,8 @@ usp_status blockattn_fwd(const void* q, const void* k, const void* v,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace blockattn_fwd needs for these sizes (0 for F32). */
-usp_status blockattn_fwd_workspace_size(int64_t Sk, int32_t Hkv, int32_t D, usp_dtype in_dtype,
-                                        size_t* bytes);
+usp_status blockattn_fwd_workspace_size(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D,
+                                        usp_dtype in_dtype, size_t* bytes);
 
 /* Bytes of device workspace blockattn_bwd needs for these sizes. */
 usp_status blockattn_bwd_workspace_size(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D,

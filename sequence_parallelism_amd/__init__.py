@@ -34,8 +34,8 @@ SIGNATURES = {
                                      _c_int32, _vp, _c_int64, _c_int64, _c_int32, _c_float,
                                      ctypes.c_int, _vp, ctypes.c_int, _vp, _c_int64, _vp,
                                      ctypes.c_size_t, _vp]),
-    "blockattn_fwd_workspace_size": (ctypes.c_int, [_c_int64, _c_int32, _c_int32, ctypes.c_int,
-                                                    ctypes.POINTER(ctypes.c_size_t)]),
+    "blockattn_fwd_workspace_size": (ctypes.c_int, [_c_int64, _c_int64, _c_int32, _c_int32, _c_int32,
+                                                    ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
     "blockattn_bwd_workspace_size": (ctypes.c_int, [_c_int64, _c_int64, _c_int32, _c_int32,
                                                     _c_int32, ctypes.POINTER(ctypes.c_size_t)]),
     "blockattn_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_int64, _vp, _c_int64, _c_int64,
@@ -145,11 +145,11 @@ def head_to_seq(src, P, H, out=None, group=-1, stream=None):
 
 # ---- attention --------------------------------------------------------------------
 
-def fwd_workspace_bytes(Sk, Hkv, D, dtype_code=BF16):
+def fwd_workspace_bytes(Sq, Sk, Hq, Hkv, D, dtype_code=BF16):
     lib = load()
     n = ctypes.c_size_t(0)
     _check("blockattn_fwd_workspace_size",
-           lib.blockattn_fwd_workspace_size(Sk, Hkv, D, dtype_code, ctypes.byref(n)))
+           lib.blockattn_fwd_workspace_size(Sq, Sk, Hq, Hkv, D, dtype_code, ctypes.byref(n)))
     return n.value
 
 
@@ -172,7 +172,7 @@ def blockattn_fwd(q, k, v, position_ids=None, q_start=0, k_start=0, causal=True,
         _need(position_ids, "position_ids")
         if position_ids.dtype != torch.int32:
             raise TypeError("position_ids must be int32")
-    need = fwd_workspace_bytes(Sk, Hkv, D, _dtype_code(q))
+    need = fwd_workspace_bytes(Sq, Sk, Hq, Hkv, D, _dtype_code(q))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libusp.so")
 SOURCES = ["usp_abi.hip", "permute.hip", "merge.hip", "transpose.hip", "attn_fwd.hip", "attn_bwd.hip",
-           "attn_bwd_dq.hip"]
+           "attn_bwd_dq.hip", "schedule.hip"]
 
 # gfx950 only; packed-FP32 VALU instructions disabled.
 HIPCC_FLAGS = [

@@ -79,8 +79,10 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, hi = lane >> 5;
+  // key blocks start heaviest first (schedule.hip); heads of one block are adjacent
   const int hk = blockIdx.x % f.Hkv;
-  const int k0 = (int)(blockIdx.x / f.Hkv) * BKV;      // local first key of the block
+  const int n_kb = (f.Sk + BKV - 1) / BKV;              // the order is a permutation of [0, n_kb)
+  const int k0 = min(max(a.kv_order[blockIdx.x / f.Hkv], 0), n_kb - 1) * BKV;   // first key
   const int kw0 = k0 + wave * 32;                       // this wave's first key
   const int kl = kw0 + r32;                             // this lane's key (B-operand column)
   const bool key_ok = kl < f.Sk;
@@ -199,14 +201,21 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
     p_q0 = q0;
   };
   auto store_scalars = [&](int buf) {
+    // every wave consumes its loads here, so that none is left in flight on any path
+    // (the compiler would otherwise wait for all memory traffic before reusing them)
+    asm volatile("" :: "v"(p_lse), "v"(p_delta), "v"(p_pos));
+    const int r = p_q0 + lane;
+    const bool ok = r < f.Sq;
+    const int g = f.q_start + r;
+    const float l2 = ok ? p_lse * USP_LOG2E : 0.f;
+    const float dl = ok ? p_delta : 0.f;
+    const int dsv = !ok ? 0x7fffffff : (f.causal ? g - p_pos : -0x7fffffff);
+    const int gqv = !ok ? -0x7fffffff : (f.causal ? g : 0x7fffffff);
     if (wave == 0) {
-      const int r = p_q0 + lane;
-      const bool ok = r < f.Sq;
-      const int g = f.q_start + r;
-      lse2_s[buf][lane] = ok ? p_lse * USP_LOG2E : 0.f;
-      delta_s[buf][lane] = ok ? p_delta : 0.f;
-      dsq_s[buf][lane] = !ok ? 0x7fffffff : (f.causal ? g - p_pos : -0x7fffffff);
-      gq_s[buf][lane] = !ok ? -0x7fffffff : (f.causal ? g : 0x7fffffff);
+      lse2_s[buf][lane] = l2;
+      delta_s[buf][lane] = dl;
+      dsq_s[buf][lane] = dsv;
+      gq_s[buf][lane] = gqv;
     }
   };
 
@@ -379,7 +388,11 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
 }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
-
+size_t n_kv_blocks(int64_t Sk) { return (size_t)((Sk + BKV - 1) / BKV); }
+size_t n_dq_tiles(int64_t Sq) {
+  const int64_t br = attn_bwd_dq_rows_per_tile();
+  return (size_t)((Sq + br - 1) / br);
+}
 
 }  // namespace
 
@@ -388,7 +401,9 @@ size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv,
   const size_t sk_pad = (size_t)transpose_perm16_padded_len(Sk);
   return align256((size_t)Sq * Hq * sizeof(float))                       // D
          + 2 * align256((size_t)Hq * D * sq_pad * sizeof(bf16))           // q^T, dout^T
-         + align256((size_t)Hkv * D * sk_pad * sizeof(bf16));             // k^T
+         + align256((size_t)Hkv * D * sk_pad * sizeof(bf16))              // k^T
+         + align256(n_kv_blocks(Sk) * sizeof(int))                        // key-block order
+         + n_dq_tiles(Sq) * sizeof(int);                                  // dQ tile order
 }
 
 void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
@@ -403,6 +418,10 @@ void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
   a.dot = p;
   p += align256((size_t)f.Hq * HD * a.sq_pad * sizeof(bf16));
   a.kt = p;
+  p += align256((size_t)f.Hkv * HD * a.sk_pad * sizeof(bf16));
+  a.kv_order = reinterpret_cast<int*>(p);
+  p += align256(n_kv_blocks(f.Sk) * sizeof(int));
+  a.dq_order = reinterpret_cast<int*>(p);
 }
 
 bool attn_bwd_supported(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv) {
@@ -429,6 +448,8 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const int n_ktiles = (f.Sk + BKV - 1) / BKV;
     const int n_qtiles = (f.Sq + BQ - 1) / BQ;
+    e = launch_schedule_kv_blocks(f, n_ktiles, BKV, BQ, a.kv_order, stream);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_bwd_main_kernel, dim3((unsigned)(n_ktiles * f.Hkv)), dim3(NWB * 64), 0,
                        stream, a, n_qtiles);
   }

@@ -42,12 +42,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, hi = lane >> 5;
   // XCD-aware order (as in the forward): the workgroups an XCD runs back to back are
-  // the query heads of one query tile, tiles taken every NXCD-th from the longest
-  // causal rows down
+  // the query heads of one query tile, tiles taken every NXCD-th in decreasing order of
+  // work (schedule.hip)
   const int xcd = blockIdx.x % NXCD, j = blockIdx.x / NXCD;
   const int h = j % f.Hq;
-  const int qt = n_qtiles - 1 - ((j / f.Hq) * NXCD + xcd);
-  if (qt < 0) return;                                       // grid padding (whole workgroup)
+  const int rank = (j / f.Hq) * NXCD + xcd;
+  if (rank >= n_qtiles) return;                             // grid padding (whole workgroup)
+  const int qt = min(max(a.dq_order[rank], 0), n_qtiles - 1);   // a permutation of the tiles
   const int hk = h / (f.Hq / f.Hkv);
   const int row = qt * BR + wave * 32 + r32;
   const bool row_ok = row < f.Sq;
@@ -238,10 +239,14 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
 
 // a must carry the workspace regions of attn_bwd_workspace_layout, with D and the
 // head-dim-major k already written (launch_attn_bwd_bf16 does both first).
+int attn_bwd_dq_rows_per_tile() { return BR; }
+
 hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, hipStream_t stream) {
   const AttnArgs& f = a.f;
   if (f.Sq == 0) return hipSuccess;
   const int n_qtiles = (f.Sq + BR - 1) / BR;
+  hipError_t e = launch_schedule_q_tiles(f, n_qtiles, BR, a.dq_order, stream);
+  if (e != hipSuccess) return e;
   dim3 grid((unsigned)(((n_qtiles + NXCD - 1) / NXCD) * NXCD * f.Hq));
   hipLaunchKernelGGL(attn_bwd_dq_kernel, grid, dim3(NW * 64), 0, stream, a, n_qtiles);
   return hipGetLastError();

@@ -94,12 +94,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   const int r32 = lane & 31, hi = lane >> 5;
   // XCD-aware order: the workgroups an XCD runs back to back are the query heads
   // of one query tile (heads sharing a key/value head are adjacent), tiles taken
-  // every NXCD-th from the longest causal rows down, so concurrent workgroups on an
-  // XCD read the same key/value tiles from its L2 and every XCD gets a fair share.
+  // every NXCD-th in decreasing order of work (schedule.hip), so concurrent
+  // workgroups on an XCD read the same key/value tiles from its L2, every XCD gets a
+  // fair share, and the heaviest tiles start first.
   const int xcd = blockIdx.x % NXCD, j = blockIdx.x / NXCD;
   const int h = j % a.Hq;
-  const int qt = n_qtiles - 1 - ((j / a.Hq) * NXCD + xcd);
-  if (qt < 0) return;                                       // grid padding (whole workgroup)
+  const int rank = (j / a.Hq) * NXCD + xcd;
+  if (rank >= n_qtiles) return;                             // grid padding (whole workgroup)
+  const int qt = min(max(a.q_order[rank], 0), n_qtiles - 1);   // a permutation of the tiles
   const int hk = h / (a.Hq / a.Hkv);
   const int row = qt * BR + wave * 32 + r32;
   const bool row_ok = row < a.Sq;
@@ -337,9 +339,23 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
-size_t attn_fwd_workspace_bytes(int64_t Sk, int32_t Hkv, int32_t D, int bf16_path) {
+namespace {
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+}  // namespace
+
+// workspace: V^T copy [Hkv][D][padded Sk] bf16, then the query-tile order
+size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hkv, int32_t D, int bf16_path) {
   if (!bf16_path) return 0;
-  return (size_t)Hkv * D * transpose_perm16_padded_len(Sk) * sizeof(bf16);
+  const size_t n_qtiles = (size_t)((Sq + BR - 1) / BR);
+  return align256((size_t)Hkv * D * transpose_perm16_padded_len(Sk) * sizeof(bf16)) +
+         n_qtiles * sizeof(int);
+}
+
+void attn_fwd_workspace_layout(AttnArgs& a, void* base) {
+  char* p = reinterpret_cast<char*>(base);
+  a.vt = p;
+  a.vt_ld = transpose_perm16_padded_len(a.Sk);
+  a.q_order = reinterpret_cast<int*>(p + align256((size_t)a.Hkv * a.D * a.vt_ld * sizeof(bf16)));
 }
 
 // a.vt must point at a workspace of attn_fwd_workspace_bytes; it is filled here.
@@ -350,6 +366,8 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t stream
     if (e != hipSuccess) return e;
   }
   const int n_qtiles = (a.Sq + BR - 1) / BR;
+  hipError_t e = launch_schedule_q_tiles(a, n_qtiles, BR, a.q_order, stream);
+  if (e != hipSuccess) return e;
   dim3 grid((unsigned)(((n_qtiles + NXCD - 1) / NXCD) * NXCD * a.Hq));
   if (o_f32)
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, grid, dim3(NW * 64), 0, stream, a, n_qtiles);

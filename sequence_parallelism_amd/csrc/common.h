@@ -45,9 +45,12 @@ struct AttnArgs {
   float scale;
   const void* vt;      // bf16 path: V in head-dim-major layout (see transpose.hip)
   int64_t vt_ld;       // its padded token length
+  int* q_order;        // bf16 path: query tiles heaviest first (schedule.hip)
 };
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t s);
-size_t attn_fwd_workspace_bytes(int64_t Sk, int32_t Hkv, int32_t D, int bf16_path);
+size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hkv, int32_t D, int bf16_path);
+// fills a.vt, a.vt_ld and a.q_order from the workspace base (bf16 path)
+void attn_fwd_workspace_layout(AttnArgs& a, void* base);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t s);
 
 struct AttnBwdArgs {
@@ -61,6 +64,8 @@ struct AttnBwdArgs {
   void* qt;            // [Hq][D][sq_pad] bf16, head-dim-major q (transpose.hip order)
   void* dot;           // [Hq][D][sq_pad] bf16, head-dim-major dout
   void* kt;            // [Hkv][D][sk_pad] bf16, head-dim-major k
+  int* kv_order;       // key blocks of the dK/dV kernel, heaviest first
+  int* dq_order;       // query tiles of the dQ kernel, heaviest first
   int64_t sq_pad, sk_pad;
 };
 size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D);
@@ -71,6 +76,13 @@ bool attn_bwd_supported(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv);
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s);
 // the query-stationary dQ kernel (attn_bwd_dq.hip), launched by launch_attn_bwd_bf16
 hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, hipStream_t s);
+int attn_bwd_dq_rows_per_tile();
+
+// Heaviest-first launch orders (schedule.hip): key blocks of bkv keys seen by bq-row
+// query tiles (dK/dV kernel), and query tiles of br rows (forward and dQ kernels).
+hipError_t launch_schedule_kv_blocks(const AttnArgs& a, int n_blocks, int bkv, int bq, int* order,
+                                     hipStream_t s);
+hipError_t launch_schedule_q_tiles(const AttnArgs& a, int n_tiles, int br, int* order, hipStream_t s);
 
 // Y[h][d][p] = X[tok(p)][h][d] over a padded token axis, 16-token groups permuted
 // to MFMA slot order (transpose.hip); D = 128, bf16.

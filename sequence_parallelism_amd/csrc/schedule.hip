@@ -1,0 +1,118 @@
+// Heaviest-first launch order for the attention kernels (longest-processing-time-first
+// list scheduling).  The hardware starts workgroups in index order on whichever CU
+// frees up; with packed documents the work per workgroup varies by orders of
+// magnitude (a causal key block at the start of a long document sees every later
+// query tile of it, one near its end sees a few), and in natural order the last
+// heavy workgroups start late and run alone.  Launching them in decreasing order of
+// work keeps every CU busy to the end.
+//
+// One workgroup per call: each unit's work (its number of visible tiles) comes from
+// position_ids the same way the kernels derive their tile ranges; units are then
+// bucket-sorted by work, heaviest first, into an int32 order array.  Units of equal
+// bucket keep no particular order; results never depend on the order.
+#include "common.h"
+
+namespace {
+
+constexpr int NT = 1024;        // threads of the one workgroup
+constexpr int NB = 2048;        // work buckets
+constexpr int MAXU = 12288;     // units sorted in LDS; larger launches keep natural order
+
+// Work of key block b of BKV keys for the dK/dV kernel: the number of BQ-row query
+// tiles that can see it (the kernel visits these for every query head of the group).
+__device__ int kv_block_work(const AttnArgs& f, int b, int bkv, int bq, int n_qtiles) {
+  if (!f.causal) return n_qtiles;
+  const int k0 = b * bkv;
+  const int gk_first = f.k_start + k0;
+  const int gk_last = f.k_start + min(k0 + bkv, f.Sk) - 1;
+  const int t0 = min(max(gk_first - f.q_start, 0) / bq, n_qtiles);
+  int lo = t0, hi = n_qtiles;   // first tile whose first row starts its document after gk_last
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const int g = f.q_start + mid * bq;
+    if (g - f.pos[g] > gk_last) hi = mid; else lo = mid + 1;
+  }
+  return lo - t0;
+}
+
+// Work of query tile t of BR rows for the forward and dQ kernels: the number of keys
+// its rows can see, from the first row's document start to the last row.
+__device__ int q_tile_work(const AttnArgs& f, int t, int br) {
+  if (!f.causal) return f.Sk;
+  const int r0 = t * br, r1 = min(r0 + br, f.Sq) - 1;
+  const int g0 = f.q_start + r0, g1 = f.q_start + r1;
+  const int lo = max(g0 - f.pos[g0], f.k_start);
+  const int hiex = min(g1 + 1, f.k_start + f.Sk);
+  return max(hiex - lo, 0);
+}
+
+// KIND 0: key blocks (p0 = keys per block, p1 = rows per query tile, p2 = query tiles);
+// KIND 1: query tiles (p0 = rows per tile).
+template <int KIND>
+__global__ __launch_bounds__(NT) void schedule_kernel(AttnArgs f, int n, int p0, int p1, int p2,
+                                                      int* __restrict__ order) {
+  __shared__ int w_s[MAXU];
+  __shared__ int start[NB];
+  __shared__ int wmax_s;
+  const int tid = threadIdx.x;
+  if (n > MAXU) {
+    for (int u = tid; u < n; u += NT) order[u] = u;
+    return;
+  }
+  for (int b = tid; b < NB; b += NT) start[b] = 0;
+  if (tid == 0) wmax_s = 0;
+  __syncthreads();
+  int wmax = 0;
+  for (int u = tid; u < n; u += NT) {
+    const int w = KIND == 0 ? kv_block_work(f, u, p0, p1, p2) : q_tile_work(f, u, p0);
+    w_s[u] = w;
+    wmax = max(wmax, w);
+  }
+  atomicMax(&wmax_s, wmax);
+  __syncthreads();
+  const int64_t wm = max(wmax_s, 1);
+  // bucket NB-1-x for work in the x-th slice from the top, so ascending bucket index is
+  // descending work
+  auto bucket = [&](int w) { return NB - 1 - (int)(((int64_t)w * (NB - 1)) / wm); };
+  for (int u = tid; u < n; u += NT) atomicAdd(&start[bucket(w_s[u])], 1);
+  __syncthreads();
+  // exclusive prefix sum of the bucket counts (two buckets per thread, Hillis-Steele
+  // over the per-thread pairs)
+  static_assert(NB == 2 * NT, "two buckets per thread");
+  const int c0 = start[2 * tid], c1 = start[2 * tid + 1];
+  int incl = c0 + c1;
+  __syncthreads();
+  start[2 * tid] = incl;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {
+    const int add = tid >= off ? start[2 * (tid - off)] : 0;
+    __syncthreads();
+    incl += add;
+    start[2 * tid] = incl;
+    __syncthreads();
+  }
+  const int excl = incl - c0 - c1;
+  __syncthreads();
+  start[2 * tid] = excl;
+  start[2 * tid + 1] = excl + c0;
+  __syncthreads();
+  for (int u = tid; u < n; u += NT) order[atomicAdd(&start[bucket(w_s[u])], 1)] = u;
+}
+
+}  // namespace
+
+hipError_t launch_schedule_kv_blocks(const AttnArgs& a, int n_blocks, int bkv, int bq, int* order,
+                                     hipStream_t stream) {
+  if (n_blocks <= 0) return hipSuccess;
+  const int n_qtiles = (a.Sq + bq - 1) / bq;
+  hipLaunchKernelGGL(schedule_kernel<0>, dim3(1), dim3(NT), 0, stream, a, n_blocks, bkv, bq, n_qtiles,
+                     order);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule_q_tiles(const AttnArgs& a, int n_tiles, int br, int* order,
+                                   hipStream_t stream) {
+  if (n_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(schedule_kernel<1>, dim3(1), dim3(NT), 0, stream, a, n_tiles, br, 0, 0, order);
+  return hipGetLastError();
+}

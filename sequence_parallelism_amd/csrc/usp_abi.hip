@@ -65,6 +65,7 @@ AttnArgs make_args(const void* q, const void* k, const void* v, int64_t Sq, int6
   a.scale = scale;
   a.vt = nullptr;
   a.vt_ld = 0;
+  a.q_order = nullptr;
   return a;
 }
 
@@ -105,12 +106,12 @@ usp_status usp_head_to_seq_permute(void* dst, const void* src, int32_t P, int64_
   return hip_status(launch_permute(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
-usp_status blockattn_fwd_workspace_size(int64_t Sk, int32_t Hkv, int32_t D, usp_dtype in_dtype,
-                                        size_t* bytes) {
+usp_status blockattn_fwd_workspace_size(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D,
+                                        usp_dtype in_dtype, size_t* bytes) {
   if (!bytes) return USP_ERR_NULL_POINTER;
   if (bad_dtype(in_dtype)) return USP_ERR_BAD_DTYPE;
-  if (Sk < 0 || Hkv < 1 || D < 1) return USP_ERR_BAD_SHAPE;
-  *bytes = attn_fwd_workspace_bytes(Sk, Hkv, D, in_dtype == USP_BF16);
+  if (Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1) return USP_ERR_BAD_SHAPE;
+  *bytes = attn_fwd_workspace_bytes(Sq, Sk, Hkv, D, in_dtype == USP_BF16);
   return USP_OK;
 }
 
@@ -124,14 +125,13 @@ usp_status blockattn_fwd(const void* q, const void* k, const void* v, int64_t Sq
   if (st != USP_OK) return st;
   if (bad_dtype(o_dtype) || (in_dtype == USP_F32 && o_dtype != USP_F32)) return USP_ERR_BAD_DTYPE;
   if (o_dtype == USP_F32 && !aligned(o, 16) && in_dtype == USP_BF16) return USP_ERR_MISALIGNED;
-  const size_t need = attn_fwd_workspace_bytes(Sk, Hkv, D, in_dtype == USP_BF16);
+  const size_t need = attn_fwd_workspace_bytes(Sq, Sk, Hkv, D, in_dtype == USP_BF16);
   if (need > 0 && !workspace) return USP_ERR_NULL_POINTER;
   if (workspace && !aligned(workspace, 16)) return USP_ERR_MISALIGNED;
   if (workspace_bytes < need) return USP_ERR_WORKSPACE_TOO_SMALL;
   AttnArgs a = make_args(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal,
                          softmax_scale, o, lse, lse_ld);
-  a.vt = workspace;
-  a.vt_ld = transpose_perm16_padded_len(Sk);
+  if (in_dtype == USP_BF16) attn_fwd_workspace_layout(a, workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (in_dtype == USP_BF16) return hip_status(launch_attn_fwd_bf16(a, o_dtype == USP_F32, s));
   return hip_status(launch_attn_fwd_f32(a, s));

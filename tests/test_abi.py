@@ -92,11 +92,11 @@ def test_fwd_validation(lib):
     assert _fwd(lib, q=A + 2) == MISAL
     assert _fwd(lib, qs=(1 << 31) - 10) == UNSUP        # global index past int32
     n = ctypes.c_size_t(0)
-    assert lib.blockattn_fwd_workspace_size(256, 1, 128, 0, ctypes.byref(n)) == OK and n.value > 0
+    assert lib.blockattn_fwd_workspace_size(256, 256, 4, 1, 128, 0, ctypes.byref(n)) == OK and n.value > 0
     assert _fwd(lib, ws_bytes=n.value - 1) == WS
     assert _fwd(lib, ws=None) == NULLP
     assert _fwd(lib, ws=A + 8) == MISAL
-    assert lib.blockattn_fwd_workspace_size(256, 1, 16, 1, ctypes.byref(n)) == OK and n.value == 0
+    assert lib.blockattn_fwd_workspace_size(256, 256, 4, 1, 16, 1, ctypes.byref(n)) == OK and n.value == 0
 
 
 def test_bwd_validation(lib):
