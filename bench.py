@@ -50,7 +50,43 @@ def parse():
                     help="skip the stand-alone permute and merge measurements")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain device copy of CALIB_BYTES (calibrates the HBM "
+                         "byte counters of a profiling run)")
     return ap.parse_args()
+
+
+CALIB_BYTES = 512 << 20        # bytes read (and written) by the calibration copy
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "attn_packed128k_traffic.md")
+
+
+def kernel_source_hash():
+    """sha1 over the HIP sources; a traffic figure counts only for the sources it was
+    measured on."""
+    import hashlib
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sequence_parallelism_amd", "csrc")
+    h = hashlib.sha1()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(d, name), "rb") as fh:
+                h.update(name.encode() + fh.read())
+    return h.hexdigest()[:12]
+
+
+def measured_traffic(call):
+    """HBM bytes per call of `call` ('fwd' or 'bwd') from the committed counter summary,
+    or None when it is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if line.startswith("traffic_bytes_per_call:"):
+                    kv = dict(t.split("=") for t in line.split(":", 1)[1].split())
+                    if kv.get("src_hash") == kernel_source_hash() and call in kv:
+                        return int(kv[call])
+    except (OSError, ValueError):
+        pass
+    return None
 
 
 def main():
@@ -164,14 +200,26 @@ def main():
         "visible_pairs_per_head": vis,
     }
 
-    # dominant launch: the backward call (its three kernels, timed together)
+    # dominant launch: the backward call, its kernels timed together by the events around
+    # it on the launch stream
     dominant = "bwd" if comp_ms["bwd"] >= comp_ms["fwd"] else "fwd"
     dom_flop = bwd_flop if dominant == "bwd" else fwd_flop
     achieved = dom_flop / (comp_ms[dominant] / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": "blockattn_bwd (pre + main + post launches)" if dominant == "bwd"
-                else "blockattn_fwd"}
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dominant),
+                "kernel": "blockattn_bwd call: D pre-pass, head-dim-major copies, launch-order "
+                          "schedules, dK/dV kernel, dQ kernel" if dominant == "bwd"
+                else "blockattn_fwd call: V^T copy, launch-order schedule, attention kernel"}
+
+    if args.calib_copy:
+        src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if not args.no_extras:
         components.update(extra_measurements(torch, usp, dev, g))
