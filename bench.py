@@ -299,6 +299,104 @@ def extra_measurements(torch, usp, dev, g):
     res["lse_merge_GBps"] = round(nbytes / (ms / 1e3) / 1e9, 1)
     res["lse_merge_frac_of_hbm_peak"] = round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
     res["lse_merge_us"] = round(ms * 1e3, 2)
+    del acc, acc_l, parts, pl
+    res.update(ring_measurement(torch, usp, dev, g))
+    res.update(allgather_measurement(torch, usp, dev, g))
+    return res
+
+
+def timed(torch, fn, reps=1):
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def ring_measurement(torch, usp, dev, g):
+    """The 256K single-document ring emulated on one GPU: query block i (16384 rows,
+    2 heads) against key blocks 0..i, fp32 partials merged by lse_merge (136 block
+    pairs); then the backward over the same pairs with the merged O and LSE.  The
+    summing of partial gradients across pairs (torch additions) is not timed."""
+    S, H, nb = 262144, 2, 16
+    blk = S // nb
+    mk = lambda: torch.randn((S, H, D), generator=g, device=dev).to(torch.bfloat16)
+    q, k, v, do = mk(), mk(), mk(), mk()
+    pos = torch.arange(S, dtype=torch.int32, device=dev)
+    acc = torch.zeros((S, H, D), dtype=torch.float32, device=dev)
+    acc_l = torch.full((H, S), -float("inf"), dtype=torch.float32, device=dev)
+    po = torch.empty((blk, H, D), dtype=torch.float32, device=dev)
+    pl = torch.empty((H, blk), dtype=torch.float32, device=dev)
+    wsf = torch.empty(usp.fwd_workspace_bytes(blk, blk, H, H, D), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(usp.bwd_workspace_bytes(blk, blk, H, H, D), dtype=torch.uint8, device=dev)
+    pq = torch.empty((blk, H, D), dtype=torch.bfloat16, device=dev)
+    pk, pv = torch.empty_like(pq), torch.empty_like(pq)
+    o = torch.empty((S, H, D), dtype=torch.bfloat16, device=dev)
+
+    def fwd():
+        acc.zero_()
+        acc_l.fill_(-float("inf"))
+        for i in range(nb):
+            qs = slice(i * blk, (i + 1) * blk)
+            for j in range(i + 1):
+                ks = slice(j * blk, (j + 1) * blk)
+                usp.blockattn_fwd(q[qs], k[ks], v[ks], pos, q_start=i * blk, k_start=j * blk,
+                                  o=po, lse=pl, workspace=wsf)
+                usp.lse_merge(acc[qs], acc_l[:, qs], po, pl)
+
+    def bwd():
+        for i in range(nb):
+            qs = slice(i * blk, (i + 1) * blk)
+            for j in range(i + 1):
+                ks = slice(j * blk, (j + 1) * blk)
+                usp.blockattn_bwd(q[qs], k[ks], v[ks], o[qs], acc_l[:, qs], do[qs], pos,
+                                  q_start=i * blk, k_start=j * blk, dq=pq, dk=pk, dv=pv,
+                                  workspace=wsb)
+
+    ms_f = timed(torch, fwd)
+    o.copy_(acc)
+    ms_b = timed(torch, bwd)
+    flop_f = 4.0 * D * (S * (S + 1) // 2) * H
+    return {"ring256k_fwd_ms": round(ms_f, 2), "ring256k_fwd_TFLOPs": round(flop_f / ms_f / 1e9, 1),
+            "ring256k_bwd_ms": round(ms_b, 2),
+            "ring256k_bwd_TFLOPs": round(2.5 * flop_f / ms_b / 1e9, 1)}
+
+
+def allgather_measurement(torch, usp, dev, g):
+    """The 32-head, S = 32768 layer (8 key/value heads, one causal document) under the
+    two decompositions, each GPU's compute emulated on this one: Ulysses (rank 0's 4
+    query heads over all 32768 tokens) and all-gather-KV (rank r's 4096 rows of all 32
+    heads against the full K, V).  The slowest rank sets the layer's pace."""
+    S, P, Hq, Hkv = 32768, 8, 32, 8
+    n = S // P
+    mk = lambda *shape: torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+    pos = torch.arange(S, dtype=torch.int32, device=dev)
+    res = {}
+    # Ulysses share: [S][4][128] q, [S][1][128] k, v
+    q, k, v, do = mk(S, Hq // P, D), mk(S, Hkv // P, D), mk(S, Hkv // P, D), mk(S, Hq // P, D)
+    o, lse = usp.blockattn_fwd(q, k, v, pos)
+
+    def uly():
+        usp.blockattn_fwd(q, k, v, pos, o=o, lse=lse)
+        usp.blockattn_bwd(q, k, v, o, lse, do, pos)
+    res["cmp32k_ulysses_share_fwd_bwd_ms"] = round(timed(torch, uly, 3), 3)
+    # all-gather-KV: rank r's rows of all heads
+    q, k, v, do = mk(S, Hq, D), mk(S, Hkv, D), mk(S, Hkv, D), mk(S, Hq, D)
+    per_rank = []
+    for r in (0, P - 1):
+        rs = slice(r * n, (r + 1) * n)
+        o, lse = usp.blockattn_fwd(q[rs], k, v, pos, q_start=r * n)
+
+        def ag():
+            usp.blockattn_fwd(q[rs], k, v, pos, q_start=r * n, o=o, lse=lse)
+            usp.blockattn_bwd(q[rs], k, v, o, lse, do[rs], pos, q_start=r * n)
+        per_rank.append(round(timed(torch, ag, 3), 3))
+    res["cmp32k_allgather_rank0_fwd_bwd_ms"] = per_rank[0]
+    res["cmp32k_allgather_rank7_fwd_bwd_ms"] = per_rank[1]
     return res
 
 

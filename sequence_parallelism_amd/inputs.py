@@ -97,9 +97,12 @@ def packed_128k():
     return q, k, v, do, pos, lengths
 
 
-def ring_256k():
+def ring_256k(with_do=False):
+    """q, k, v (and, drawn after them, dO) of the 256K single-document ring case."""
     c = RING_256K
     g = generator(c["seed"])
     shp = (c["S"], c["H"], c["D"])
     q, k, v = (normal(shp, g) for _ in range(3))
+    if with_do:
+        return q, k, v, normal(shp, g), position_ids([c["S"]])
     return q, k, v, position_ids([c["S"]])
