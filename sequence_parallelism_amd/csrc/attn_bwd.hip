@@ -46,6 +46,16 @@ constexpr int TILE = BQ * HD;       // elements of one staged tile (16 KB)
 static_assert(TILE / 8 == 4 * NWB * 64, "a staged tile is four 64-lane DMA loads per wave");
 static_assert(BQ == 64, "one lane per query row stages the row scalars");
 
+// acc += A B with the accumulator pinned to AGPRs (the dK^T, dV^T accumulators stay
+// there for the whole kernel, leaving the VGPRs to everything else).  Issued as
+// inline assembly, so the compiler inserts no MFMA wait states around it: the
+// operands' producers are far ahead (B by at least eight MFMA steps, A by a waited
+// LDS read), the s_nop covers a VALU write right before, and the accumulators are
+// read only after the padding that follows the item loops.
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 // ---- 1. D = rowsum(dO * O) -------------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -327,8 +337,8 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
               // k-slot s of lane half hi in row chunk c is row 16c + 8(s/4) + 4hi + s%4,
               // which matches P / dS element 8(c%2) + s of block c/2
               constexpr int qb = slot - 2, cc = j >> 3, db = (j >> 1) & 3;
-              if constexpr (j & 1) dka[db] = mfma32(op, sb[qb][cc], dka[db]);
-              else dva[db] = mfma32(op, pb[qb][cc], dva[db]);
+              if constexpr (j & 1) mfma32_acc(dka[db], op, sb[qb][cc]);
+              else mfma32_acc(dva[db], op, pb[qb][cc]);
             }
           },
           [&](auto I) {   // work hidden behind MFMA i
@@ -366,6 +376,8 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   for (int it = 0; it < n_full; ++it) run_item(IC<0>{}, it);
 #pragma unroll 1
   for (int it = n_full; it < n_items; ++it) run_item(IC<1>{}, it);
+  // the last accumulations (inline-assembly MFMAs) complete before any read below
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   // ---- dK = scale dK^T, dV = dV^T (bf16), lane: key kl, d = 32db + 8g4 + 4hi + 0..3
   if (key_ok) {
     const int64_t base = ((int64_t)kl * f.Hkv + hk) * HD;
