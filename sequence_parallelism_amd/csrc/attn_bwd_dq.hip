@@ -16,7 +16,9 @@
 //   * S^T = K Q^T and dP^T = V dO^T come out with one query per lane (32 MFMAs,
 //     two interleaved accumulator chains each); P and dS are formed in registers and
 //     dS^T (bf16) feeds dQ^T += K^T dS^T directly (16 MFMAs);
-//   * tiles fully visible to a wave skip the per-element mask.
+//   * tiles fully visible to a wave skip the per-element mask;
+//   * a wave raises its priority (s_setprio) while it issues MFMAs, so the other
+//     wave of its SIMD overlaps its softmax with them.
 #include "gfx950.h"
 
 namespace {
@@ -159,6 +161,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
     // ---- S^T and dP^T: 64 keys x 32 queries each.  MFMA i: S (even i) or dP (odd i)
     // of key block kb2 = (i/2)%2, d chunk kk = i/4; the next tile's DMA rides along --
     f32x16 sacc[2], dpacc[2];
+    __builtin_amdgcn_s_setprio(2);
     mfma_pipeline<PF, 32>(
         [&](auto I) {
           constexpr int i = decltype(I)::v, kb2 = (i >> 1) & 1, kk = i >> 2;
@@ -175,6 +178,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
           if constexpr (i % 4 == 1 && i / 4 < 6) dma_step(i / 4, ktn, buf ^ 1);
         });
 
+    __builtin_amdgcn_s_setprio(0);
     // ---- mask (boundary tiles only; wave-uniform branch) ---------------------------
     const int gk0 = f.k_start + kt;
     const bool full = (kt + BC <= ke) && (!f.causal || (gk0 + BC - 1 <= w_gqmin && gk0 >= w_dsmax));
@@ -205,6 +209,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
       }
     }
     // ---- dQ^T += K^T dS^T (MFMA i: key chunk c = i/4, head-dim block db = i%4) --------
+    __builtin_amdgcn_s_setprio(2);
     mfma_pipeline<PF, 16>(
         [&](auto I) {
           constexpr int i = decltype(I)::v, c = i >> 2, db = i & 3;
@@ -215,6 +220,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
           dqacc[db] = mfma32(op, sb[c], dqacc[db]);
         },
         [&](auto) {});
+    __builtin_amdgcn_s_setprio(0);
     wait_vmem();       // the next tile has landed in the other buffer
     __syncthreads();   // ... for every wave; this buffer is free again
   }

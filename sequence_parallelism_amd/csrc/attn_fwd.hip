@@ -13,10 +13,10 @@
 //   * key tiles of 64 keys are staged in double-buffered LDS: K row-major, and V
 //     from its head-dim-major copy (V^T, made once per call by transpose.hip), so
 //     every MFMA operand taken from LDS is ONE 16-byte read (LDS instruction issue,
-//     not bytes, is what limits narrower reads on gfx950).  The next tile is
-//     fetched into registers while the current one is computed, so one barrier per
-//     tile suffices and HBM latency is hidden behind the MFMA work; operand reads
-//     run four MFMAs ahead of their use;
+//     not bytes, is what limits narrower reads on gfx950).  The next tile comes by
+//     LDS-DMA, issued behind the current tile's score MFMAs, so one barrier per
+//     tile suffices and memory latency is hidden behind the MFMA work; operand
+//     reads run four MFMAs ahead of their use;
 //   * LDS rows are unpadded with XOR-swizzled 16-byte chunks: 16 lanes reading 16
 //     consecutive rows at one logical chunk hit all 64 banks once;
 //   * scores are formed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so
@@ -34,9 +34,11 @@
 // f32 kernel (small head dims, e.g. the four-device ring example): one wavefront
 // per (query row, head), keys visited one at a time with the same running
 // (m, l, O) recurrence in fp32 VALU arithmetic.
-#include "common.h"
+#include "gfx950.h"
 
 namespace {
+
+using namespace gfx950;
 
 constexpr int HD = 128;          // head dim of the MFMA path
 constexpr int NW = 8;            // wavefronts per workgroup
@@ -44,49 +46,14 @@ constexpr int BR = 32 * NW;      // query rows per workgroup
 constexpr int BC = 64;           // keys per LDS tile
 constexpr int PF = 4;            // LDS operand reads in flight ahead of their MFMA
 constexpr float RESCALE_TH = 8.f;  // log2 of the largest P allowed before the max moves
-constexpr int CH = BC * HD / 8 / (NW * 64);   // 16-byte chunks per thread per K (V^T) tile
-static_assert(CH * NW * 64 == BC * HD / 8, "tile staging splits evenly over threads");
+constexpr int TILE = BC * HD;    // elements of one staged tile (16 KB)
+static_assert(TILE / 8 == 2 * NW * 64, "a staged tile is two 64-lane DMA loads per wave");
 constexpr int NXCD = 8;          // MI355X dispatches workgroup i to XCD i % 8
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Swizzles of 16-byte chunks: rows of 128 bf16 (16 chunks) and of 64 bf16 (8 chunks).
-__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
-
-__device__ __forceinline__ int wave_min(int x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = min(x, __shfl_xor(x, off));
-  return x;
-}
-__device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off));
-  return x;
-}
-
-// N MFMAs whose A operand comes from LDS: PF reads stay in flight ahead of use.
-template <int N, typename Load, typename Mma>
-__device__ __forceinline__ void pipelined(Load load, Mma mma) {
-  bf16x8 ops[PF];
-#pragma unroll
-  for (int i = 0; i < PF && i < N; ++i) ops[i] = load(i);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const bf16x8 op = ops[i % PF];
-    if (i + PF < N) ops[i % PF] = load(i + PF);
-    mma(i, op);
-    __builtin_amdgcn_sched_barrier(0);   // keep PF reads in flight: the compiler would
-                                          // otherwise pull them next to their MFMA
-  }
-}
 
 template <bool O_F32>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int n_qtiles) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BC * HD];    // [key][d]
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][HD * BC];    // [d][key position]
+  // per buffer: K [64 keys][128] (swz16), V^T [128][64 positions] (swz8)
+  __shared__ __attribute__((aligned(16))) bf16 stage[2][2 * TILE];
   __shared__ int red[NW][2];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -108,8 +75,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   const int gq = a.q_start + row;
 
   const bf16* __restrict__ qp = reinterpret_cast<const bf16*>(a.q);
-  const bf16* __restrict__ kp = reinterpret_cast<const bf16*>(a.k);
-  const bf16* __restrict__ vtp = reinterpret_cast<const bf16*>(a.vt) + (int64_t)hk * HD * a.vt_ld;
 
   // ---- visible key ranges (global token indices) --------------------------------
   int ds = 0x7fffffff;
@@ -148,26 +113,28 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
     }
   }
 
-  // ---- staging: K tile [64 keys][128] and V^T tile [128][64 positions] ----------
-  bf16x8 pk[CH], pv[CH];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int c = tid + NW * 64 * u;
-      // K: key kt + c/16 (clamped to a real row; the mask zeroes it), chunk c%16
-      const int kl = min(kt + (c >> 4), a.Sk - 1);
-      pk[u] = *reinterpret_cast<const bf16x8*>(kp + ((int64_t)kl * a.Hkv + hk) * HD + (c & 15) * 8);
-      // V^T: row d = c/8, positions kt + 8*(c%8) .. +7 (the padded copy covers them)
-      pv[u] = *reinterpret_cast<const bf16x8*>(vtp + (int64_t)(c >> 3) * a.vt_ld + kt + (c & 7) * 8);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int c = tid + NW * 64 * u;
-      const int kr = c >> 4, kc = c & 15, vr = c >> 3, vc = c & 7;
-      *reinterpret_cast<bf16x8*>(&Ks[buf][kr * HD + ((kc ^ swz16(kr)) << 3)]) = pk[u];
-      *reinterpret_cast<bf16x8*>(&Vt[buf][vr * BC + ((vc ^ swz8(vr)) << 3)]) = pv[u];
+  // ---- staging by LDS-DMA: tile u (K, V^T), load i (0..1) of wave w covers physical
+  // chunks [(8i + w) * 64, +64), lane l the chunk (8i + w) * 64 + l:
+  //   K:   key row 32i + 4w + l/16, physical chunk l%16;
+  //   V^T: head-dim row 64i + 8w + l/8, physical chunk l%8.
+  // The swizzle depends on the row modulo 16 only, so one lane offset serves both loads.
+  const uint32_t kr0 = (uint32_t)(4 * wave + (lane >> 4));
+  const uint32_t k_lc = (uint32_t)((((lane & 15) ^ swz16(kr0)) << 3) * 2);
+  const uint32_t rowkB = (uint32_t)a.Hkv * HD * 2;                // bytes per k row
+  const int td0 = 8 * wave + (lane >> 3);
+  const uint32_t t_off = (uint32_t)((td0 * a.vt_ld + (((lane & 7) ^ swz8(td0)) << 3)) * 2);
+  const uint32_t stage_lds = lds_addr(&stage[0][0]);
+  auto dma_step = [&](int s, int kt, int buf) {   // s = 2u + i
+    const int u = s >> 1, i = s & 1;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        stage_lds + (uint32_t)(((buf * 2 + u) * TILE + (NW * i + wave) * 512) * 2));
+    if (u == 0) {   // keys past Sk are clamped to the last key (the mask zeroes them)
+      const uint32_t lim = (uint32_t)(a.Sk - 1 - kt);
+      const uint32_t voff = min(kr0 + 32 * i, lim) * rowkB + k_lc;
+      dma16(reinterpret_cast<const char*>(a.k) + ((int64_t)kt * a.Hkv + hk) * HD * 2, voff, lds);
+    } else {        // the padded copy covers every position of the tile
+      dma16(reinterpret_cast<const char*>(a.vt) + (((int64_t)hk * HD + 64 * i) * a.vt_ld + kt) * 2,
+            t_off, lds);
     }
   };
 
@@ -178,31 +145,41 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
 
-  // per-lane element offsets inside the tiles (swizzled)
-  //   K (A operand of S^T): row 32*kb2 + r32, logical chunk 2*kk + hi
-  //   V^T (A operand of O^T): row 32*db + r32, logical chunk 2c + hi (positions
-  //   16c + 8hi .. +7 = the lane half's eight key slots of chunk c)
-  int koff[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) koff[kk] = r32 * HD + (((2 * kk + hi) ^ swz16(r32)) << 3);
-  int voff[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) voff[c] = r32 * BC + (((2 * c + hi) ^ swz8(r32)) << 3);
+  // per-lane element offsets inside the tiles: chunk 2k + hi of row r sits at
+  // (2k + hi) ^ swz(r), i.e. at  base ^ 16k  with base = r * len + 8 (hi ^ swz(r))
+  //   K (A operand of S^T): row 32 kb2 + r32, chunks 2 kk + hi
+  //   V^T (A operand of O^T): row 32 db + r32, chunks 2c + hi (positions 16c + 8hi ..
+  //   +7 = the lane half's eight key slots of chunk c)
+  const int kbase = r32 * HD + ((hi ^ swz16(r32)) << 3);
+  const int vbase = r32 * BC + ((hi ^ swz8(r32)) << 3);
 
   if (kb < ke) {
-    load_tile(kb);
-    store_tile(0);
-    if (kb + BC < ke) load_tile(kb + BC);
+    for (int s = 0; s < 4; ++s) dma_step(s, kb, 0);
+    wait_vmem();
     __syncthreads();
   }
+  const int last_kt = kb + ((ke - kb - 1) / BC) * BC;
   int buf = 0;
   for (int kt = kb; kt < ke; kt += BC, buf ^= 1) {
-    const bf16* Kb = Ks[buf];
-    const bf16* Vb = Vt[buf];
-    // ---- S^T tile: 64 keys x 32 queries (MFMA i: key block i%2, d chunk i/2) ------
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-    pipelined<16>([&](int i) { return *reinterpret_cast<const bf16x8*>(&Kb[32 * (i & 1) * HD + koff[i >> 1]]); },
-                  [&](int i, const bf16x8& op) { sacc[i & 1] = mfma32(op, qf[i >> 1], sacc[i & 1]); });
+    const bf16* Kb = &stage[buf][0];
+    const bf16* Vb = &stage[buf][TILE];
+    const int ktn = min(kt + BC, last_kt);   // the last tile fetches itself again (unused)
+    // ---- S^T tile: 64 keys x 32 queries (MFMA i: key block i%2, d chunk i/2); the
+    // next tile's DMA rides along --------------------------------------------------
+    f32x16 sacc[2];
+    mfma_pipeline<PF, 16>(
+        [&](auto I) {
+          constexpr int i = decltype(I)::v;
+          return *reinterpret_cast<const bf16x8*>(&Kb[32 * (i & 1) * HD + (kbase ^ (16 * (i >> 1)))]);
+        },
+        [&](auto I, const bf16x8& op) {
+          constexpr int i = decltype(I)::v;
+          sacc[i & 1] = mfma32(op, qf[i >> 1], i < 2 ? f32x16{} : sacc[i & 1]);
+        },
+        [&](auto I) {
+          constexpr int i = decltype(I)::v;
+          if constexpr (i % 4 == 1) dma_step(i / 4, ktn, buf ^ 1);
+        });
     // ---- mask, row max ------------------------------------------------------------
     const int gk0 = a.k_start + kt;
     const bool full = (kt + BC <= ke) && (kt >= 0) &&
@@ -257,14 +234,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
     }
     l_run += psum;
     // ---- O^T += V^T P^T (MFMA i: key chunk c = i/4, head-dim block db = i%4) --------
-    pipelined<16>([&](int i) { return *reinterpret_cast<const bf16x8*>(&Vb[32 * (i & 3) * BC + voff[i >> 2]]); },
-                  [&](int i, const bf16x8& op) { oacc[i & 3] = mfma32(op, pb[i >> 2], oacc[i & 3]); });
-    // ---- stage the next tile into the other buffer; fetch the one after ----------
-    if (kt + BC < ke) {
-      store_tile(buf ^ 1);
-      if (kt + 2 * BC < ke) load_tile(kt + 2 * BC);
-    }
-    __syncthreads();
+    mfma_pipeline<PF, 16>(
+        [&](auto I) {
+          constexpr int i = decltype(I)::v;
+          return *reinterpret_cast<const bf16x8*>(&Vb[32 * (i & 3) * BC + (vbase ^ (16 * (i >> 2)))]);
+        },
+        [&](auto I, const bf16x8& op) {
+          constexpr int i = decltype(I)::v;
+          oacc[i & 3] = mfma32(op, pb[i >> 2], oacc[i & 3]);
+        },
+        [&](auto) {});
+    wait_vmem();       // the next tile has landed in the other buffer
+    __syncthreads();   // ... for every wave; this buffer is free again
   }
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 ---------------------------
