@@ -46,6 +46,15 @@ constexpr int TILE = BQ * HD;       // elements of one staged tile (16 KB)
 static_assert(TILE / 8 == 4 * NWB * 64, "a staged tile is four 64-lane DMA loads per wave");
 static_assert(BQ == 64, "one lane per query row stages the row scalars");
 
+// Order of the 16 S / dP MFMAs of a 32-row block (value 8 dp + kk): four S steps
+// first, so that -D (the dP accumulator's start) has arrived from LDS by the first
+// dP step, then S and dP alternate, then the last dP steps.
+__host__ __device__ constexpr int sdp_order(int j) {
+  return j < 4 ? j : j < 12 ? ((j & 1) ? 4 + (j - 5) / 2 : 8 + (j - 4) / 2) : 8 + 4 + (j - 12);
+}
+static_assert(sdp_order(4) == 8 && sdp_order(5) == 4 && sdp_order(11) == 7 && sdp_order(10) == 11 &&
+              sdp_order(12) == 12 && sdp_order(15) == 15, "S / dP order");
+
 // acc += A B with the accumulator pinned to AGPRs (the dK^T, dV^T accumulators stay
 // there for the whole kernel, leaving the VGPRs to everything else).  Issued as
 // inline assembly, so the compiler inserts no MFMA wait states around it: the
@@ -81,7 +90,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   // dO^T [128][64] (swz8) -- 4 tiles of 16 KB
   __shared__ __attribute__((aligned(16))) bf16 stage[2][4 * TILE];
   __shared__ __attribute__((aligned(16))) float lse2_s[2][BQ];
-  __shared__ __attribute__((aligned(16))) float delta_s[2][BQ];
+  __shared__ __attribute__((aligned(16))) float ndelta_s[2][BQ];   // -D
   __shared__ __attribute__((aligned(16))) int dsq_s[2][BQ];
   __shared__ __attribute__((aligned(16))) int gq_s[2][BQ];
 
@@ -218,12 +227,12 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
     const bool ok = r < f.Sq;
     const int g = f.q_start + r;
     const float l2 = ok ? p_lse * USP_LOG2E : 0.f;
-    const float dl = ok ? p_delta : 0.f;
+    const float dl = ok ? -p_delta : 0.f;   // -D: the initial dP accumulator
     const int dsv = !ok ? 0x7fffffff : (f.causal ? g - p_pos : -0x7fffffff);
     const int gqv = !ok ? -0x7fffffff : (f.causal ? g : 0x7fffffff);
     if (wave == 0) {
       lse2_s[buf][lane] = l2;
-      delta_s[buf][lane] = dl;
+      ndelta_s[buf][lane] = dl;
       dsq_s[buf][lane] = dsv;
       gq_s[buf][lane] = gqv;
     }
@@ -288,7 +297,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
       };
       auto soft_b = [&](auto QB, auto E) {
         constexpr int qb = decltype(QB)::v, e = decltype(E)::v;
-        const float ds = pv[qb][e] * (dpacc[qb][e] - e4[qb][e >> 2][e & 3]);
+        const float ds = pv[qb][e] * dpacc[qb][e];   // dP - D (the accumulator started at -D)
         if constexpr (e & 1) {
           pb[qb][e >> 3][(e & 7) - 1] = (bf16)pv[qb][e - 1];
           pb[qb][e >> 3][e & 7] = (bf16)pv[qb][e];
@@ -299,10 +308,13 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
         }
       };
       // row scalars of rows 32qb + 8g4 + 4hi + 0..3, read four steps before first use
+      auto load_nd = [&](auto QB, auto G4) {   // -D of the same rows
+        constexpr int qb = decltype(QB)::v, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
+        e4[qb][g4] = *reinterpret_cast<const f32x4*>(&ndelta_s[buf][q + 4 * hi]);
+      };
       auto load_rows = [&](auto QB, auto G4) {
         constexpr int qb = decltype(QB)::v, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
         l4[qb][g4] = *reinterpret_cast<const f32x4*>(&lse2_s[buf][q + 4 * hi]);
-        e4[qb][g4] = *reinterpret_cast<const f32x4*>(&delta_s[buf][q + 4 * hi]);
         if constexpr (MASK) {
           const int4 dsv = *reinterpret_cast<const int4*>(&dsq_s[buf][q + 4 * hi]);
           const int4 gqv = *reinterpret_cast<const int4*>(&gq_s[buf][q + 4 * hi]);
@@ -315,12 +327,14 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
           }
         }
       };
+      unroll<4>([&](auto G4) { load_nd(IC<0>{}, G4); });   // needed by block 0's first dP
       mfma_pipeline<PF, 64>(
           [&](auto I) {   // LDS operand of MFMA i
             constexpr int i = decltype(I)::v, slot = i / 16, j = i % 16;
-            if constexpr (slot < 2) {   // S (even j) / dP (odd j) of block qb = slot, k-step j/2
-              const bf16* t = (j & 1) ? Db : Qb;
-              return *reinterpret_cast<const bf16x8*>(&t[32 * slot * HD + (qbase ^ (16 * (j >> 1)))]);
+            if constexpr (slot < 2) {   // S or dP of block qb = slot, k-step kk (sdp_order)
+              constexpr int dp = sdp_order(j) >> 3, kk = sdp_order(j) & 7;
+              const bf16* t = dp ? Db : Qb;
+              return *reinterpret_cast<const bf16x8*>(&t[32 * slot * HD + (qbase ^ (16 * kk))]);
             } else {                    // dV^T (even) / dK^T (odd), row chunk c, head-dim block db
               constexpr int c = 2 * (slot - 2) + (j >> 3), db = (j >> 1) & 3;
               const bf16* t = (j & 1) ? Qtb : Dtb;
@@ -330,9 +344,19 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
           [&](auto I, const bf16x8& op) {
             constexpr int i = decltype(I)::v, slot = i / 16, j = i % 16;
             if constexpr (slot < 2) {
-              constexpr int kk = j >> 1;
-              if constexpr (j & 1) dpacc[slot] = mfma32(op, vf[kk], kk == 0 ? f32x16{} : dpacc[slot]);
-              else sacc[slot] = mfma32(op, kf[kk], kk == 0 ? f32x16{} : sacc[slot]);
+              constexpr int dp = sdp_order(j) >> 3, kk = sdp_order(j) & 7;
+              if constexpr (dp) {
+                if constexpr (kk == 0) {   // dP starts from -D of the element's row
+                  f32x16 c;
+#pragma unroll
+                  for (int e = 0; e < 16; ++e) c[e] = e4[slot][e >> 2][e & 3];
+                  dpacc[slot] = mfma32(op, vf[0], c);
+                } else {
+                  dpacc[slot] = mfma32(op, vf[kk], dpacc[slot]);
+                }
+              } else {
+                sacc[slot] = mfma32(op, kf[kk], kk == 0 ? f32x16{} : sacc[slot]);
+              }
             } else {
               // k-slot s of lane half hi in row chunk c is row 16c + 8(s/4) + 4hi + s%4,
               // which matches P / dS element 8(c%2) + s of block c/2
@@ -349,7 +373,8 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
               constexpr int qb = i < 28 ? 0 : 1, g4 = (i - 12 - 16 * qb) / 4;
               load_rows(IC<qb>{}, IC<g4>{});
             }
-            if constexpr (i % 4 == 1) dma_step(i / 4, hn, q0n, buf ^ 1, vq);   // item it+1
+            if constexpr (i >= 8 && i < 12) load_nd(IC<1>{}, IC<i - 8>{});
+            if constexpr (i % 3 == 1 && i < 48) dma_step(i / 3, hn, q0n, buf ^ 1, vq);   // item it+1
             if constexpr (i == 2) load_scalars(hn, q0n);                           // its row scalars
             // block 0's softmax behind block 1's S, dP; block 1's behind block 0's dV, dK
             if constexpr (slot == 1) {
