@@ -2,15 +2,19 @@
 
 One step = one pass of the whole hot path over one batch: the Ulysses share of a
 sequence-parallel attention layer (8 ranks, 32 query heads, 8 key/value heads,
-head dim 128) at S = 131072 tokens in 16 packed documents, as rank 0 sees it:
+head dim 128) at S = 131072 tokens in 16 packed documents, as rank 0 sees it,
+with the re-layouts fused into the attention loads and stores:
 
-  1. sequence-shard -> head-shard re-layout of x_q, x_k, x_v ([8][16384][H][128]
-     -> q [131072][4][128], k, v [131072][1][128]);
-  2. blockattn_fwd (causal over packed documents via position_ids);
-  3. head-shard -> sequence-shard re-layout of O;
-  4. re-layout of the upstream gradient dO;
-  5. blockattn_bwd;
-  6. re-layout of dQ, dK, dV back to sequence shards.
+  1. usp_ulysses_attn_fwd: reads rank 0's heads of x_q, x_k, x_v in place from
+     the sequence-sharded [8][16384][H][128] tensors (causal over packed documents
+     via position_ids) and writes its heads of O back in that layout;
+  2. usp_ulysses_attn_bwd: reads x_q, x_k, x_v, O and dO the same way and writes
+     rank 0's heads of dX_q, dX_k, dX_v.
+
+The same step through explicit re-layout kernels (seq->head permutes of x_q,
+x_k, x_v and dO, blockattn_fwd/bwd on the head-sharded share [131072][4 | 1][128],
+head->seq permutes of O and of the gradients) is timed after it and reported
+under "components" with each kernel's share of the time.
 
 The share is exactly the packed long-context attention workload (4 query heads
 sharing 1 key/value head, 16 documents with multinomial lengths).  `value` is
@@ -47,7 +51,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the stand-alone permute and merge measurements")
+                    help="skip the unfused step and the stand-alone permute, merge, ring and "
+                         "all-gather measurements (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
@@ -143,9 +148,22 @@ def main():
         "head_to_seq_grads": 2 * eb * (dq.numel() + dk.numel() + dv.numel()),
     }
     stream = torch.cuda.current_stream()
-    names = ["seq_to_head_qkv", "fwd", "head_to_seq_o", "seq_to_head_do", "bwd", "head_to_seq_grads"]
+    names_u = ["seq_to_head_qkv", "fwd", "head_to_seq_o", "seq_to_head_do", "bwd", "head_to_seq_grads"]
+    names = ["fwd", "bwd"]
 
     def step(ev=None):
+        """The fused step: the timed hot path."""
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        usp.ulysses_attn_fwd(xq, xk, xv, 0, pos, o_seq=o_seq, lse=lse, workspace=ws_f)
+        mark(1)
+        usp.ulysses_attn_bwd(xq, xk, xv, o_seq, lse, xdo, 0, pos, dxq=dxq, dxk=dxk, dxv=dxv,
+                             workspace=ws)
+        mark(2)
+
+    def step_unfused(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record(stream)
@@ -167,38 +185,52 @@ def main():
         usp.head_to_seq(dv, P, H_KV, out=dxv, group=0)
         mark(6)
 
+    def run(fn, n_marks, steps):
+        """Times `steps` calls of fn bracketed by synchronisations; per-component HIP
+        events on the launch stream."""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_marks)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return (t1 - t0) * 1e3 / steps, [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+                                         for j in range(n_marks - 1)]
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    ms_step, comp = run(step, 3, args.steps)
+    comp_ms = dict(zip(names, comp))
 
-    # per-component HIP events on the launch stream, over the timed steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    comp_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
-               for j, n in enumerate(names)}
+    ms_unfused, comp_u = None, {}
+    if not args.no_extras:
+        for _ in range(args.warmup):
+            step_unfused()
+        ms_unfused, comp = run(step_unfused, 7, args.steps)
+        comp_u = dict(zip(names_u, comp))
 
     step_s = ms_step / 1e3
     value = (fwd_flop + bwd_flop) / step_s / 1e12
     fwd_tf = fwd_flop / (comp_ms["fwd"] / 1e3) / 1e12
     bwd_tf = bwd_flop / (comp_ms["bwd"] / 1e3) / 1e12
-    perm_ms = sum(comp_ms[n] for n in perm_bytes)
-    perm_gbps = sum(perm_bytes.values()) / (perm_ms / 1e3) / 1e9
     components = {
         "ms": {n: round(v_, 4) for n, v_ in comp_ms.items()},
         "attn_fwd_TFLOPs": round(fwd_tf, 2),
         "attn_bwd_TFLOPs": round(bwd_tf, 2),
         "attn_fwd_frac_of_bf16_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
         "attn_bwd_frac_of_bf16_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
-        "permute_GBps_in_step": round(perm_gbps, 1),
-        "permute_frac_of_hbm_peak_in_step": round(perm_gbps / PEAK_HBM_GBPS, 4),
         "visible_pairs_per_head": vis,
     }
+    if comp_u:
+        perm_gbps = sum(perm_bytes.values()) / (sum(comp_u[n] for n in perm_bytes) / 1e3) / 1e9
+        components.update({
+            "unfused_step_ms": round(ms_unfused, 4),
+            "unfused_ms": {n: round(v_, 4) for n, v_ in comp_u.items()},
+            "permute_GBps_in_unfused_step": round(perm_gbps, 1),
+            "permute_frac_of_hbm_peak_in_unfused_step": round(perm_gbps / PEAK_HBM_GBPS, 4),
+        })
 
     # dominant launch: the backward call, its kernels timed together by the events around
     # it on the launch stream
@@ -208,9 +240,9 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(dominant),
-                "kernel": "blockattn_bwd call: D pre-pass, head-dim-major copies, launch-order "
+                "kernel": "usp_ulysses_attn_bwd call: D pre-pass, head-dim-major copies, launch-order "
                           "schedules, dK/dV kernel, dQ kernel" if dominant == "bwd"
-                else "blockattn_fwd call: V^T copy, launch-order schedule, attention kernel"}
+                else "usp_ulysses_attn_fwd call: V^T copy, launch-order schedule, attention kernel"}
 
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
@@ -226,6 +258,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
+        for x, y in ((xq, q), (xk, k), (xv, v), (xdo, do)):    # rank 0's share, head-sharded
+            usp.seq_to_head(x, P, group=0, out=y)
         cpu = cpu_baseline(q, k, v, do, lengths, args.cpu_seconds)
 
     out = {
@@ -235,7 +269,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "Ulysses SP=8 share, packed long context: S=131072, 16 docs "
                                "(multinomial lengths, seed 1), 4 query heads sharing 1 kv head, "
-                               "d=128, bf16; permutes + fwd + bwd",
+                               "d=128, bf16; fwd + bwd with the re-layouts fused",
                    "S": S, "Hq": hq, "Hkv": hkv, "D": D, "sp": P, "layer_heads_q": H_Q,
                    "layer_heads_kv": H_KV, "docs": N_DOCS},
         "tokens_per_s": round(S / step_s, 1),

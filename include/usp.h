@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define USP_ABI_VERSION 1
+#define USP_ABI_VERSION 2
 
 typedef enum {
   USP_OK = 0,
@@ -186,6 +186,45 @@ usp_status blockattn_bwd(const void* q, const void* k, const void* v, const void
 usp_status lse_merge(void* o_acc, usp_dtype acc_dtype, float* lse_acc, int64_t lse_acc_ld,
                      const void* o_part, usp_dtype part_dtype, const float* lse_part,
                      int64_t lse_part_ld, int64_t S, int32_t H, int32_t D, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Ulysses attention with the re-layout fused into the attention loads and stores.
+ *
+ * Keryc, "Ulysses SP: entrenar modelos con millones de tokens", section "Como
+ * funciona Ulysses Sequence Parallelism (SP)", and the DeepSpeed-Ulysses notes,
+ * section "Method": rank g holds all tokens of heads [g H/P, (g+1) H/P) between the
+ * two re-layouts.  These entry points compute exactly what usp_seq_to_head_permute
+ * (group g) + blockattn_fwd / blockattn_bwd (causal per position_ids, q_start =
+ * k_start = 0) + usp_head_to_seq_permute (group g) compute, without the permuted
+ * copies: the kernels read rank g's head slice of every shard in place.
+ *
+ *   xq [P][S_local][Hq_total][D], xk, xv [P][S_local][Hkv_total][D]   (bf16)
+ *   o_seq (output of the forward, input of the backward), xdo, dxq: laid out like
+ *   xq; dxk, dxv like xk.  Only rank g's head slice [g Hq_total/P, (g+1) Hq_total/P)
+ *   (resp. of Hkv_total) of the outputs is written; the other heads are untouched.
+ *   lse [Hq_total/P][lse_ld >= P S_local] float32, for rank g's heads, global token
+ *   order (the forward writes it, the backward reads it).
+ *   position_ids: int32 [P S_local] over the global token order.
+ *   workspace: at least blockattn_fwd_workspace_size / blockattn_bwd_workspace_size
+ *   bytes for Sq = Sk = P S_local, Hq = Hq_total/P, Hkv = Hkv_total/P (16-byte
+ *   aligned for the forward, 256-byte for the backward); contents clobbered.
+ * Supported: bf16, D = 128, S_local a multiple of 256 (USP_ERR_UNSUPPORTED
+ * otherwise; use the separate permutes then).
+ * Errors: NULL pointers; P, S_local, heads < 1 or group outside [0, P) (BAD_SHAPE);
+ * Hq_total or Hkv_total not divisible by P, or the query heads of a rank not a
+ * multiple of its key/value heads (NOT_DIVISIBLE); misaligned; workspace too small.
+ * ------------------------------------------------------------------------- */
+usp_status usp_ulysses_attn_fwd(const void* xq, const void* xk, const void* xv, int32_t P,
+                                int64_t S_local, int32_t Hq_total, int32_t Hkv_total, int32_t D,
+                                int32_t group, const int32_t* position_ids, int32_t causal,
+                                float softmax_scale, usp_dtype in_dtype, void* o_seq, float* lse,
+                                int64_t lse_ld, void* workspace, size_t workspace_bytes, void* stream);
+usp_status usp_ulysses_attn_bwd(const void* xq, const void* xk, const void* xv, const void* o_seq,
+                                const float* lse, int64_t lse_ld, const void* xdo, int32_t P,
+                                int64_t S_local, int32_t Hq_total, int32_t Hkv_total, int32_t D,
+                                int32_t group, const int32_t* position_ids, int32_t causal,
+                                float softmax_scale, usp_dtype in_dtype, void* dxq, void* dxk,
+                                void* dxv, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

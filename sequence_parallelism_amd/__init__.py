@@ -44,6 +44,13 @@ SIGNATURES = {
                                      ctypes.c_size_t, _vp]),
     "lse_merge": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _c_int64, _vp, ctypes.c_int, _vp,
                                  _c_int64, _c_int64, _c_int32, _c_int32, _vp]),
+    "usp_ulysses_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, _c_int32, _c_int64, _c_int32, _c_int32,
+                                            _c_int32, _c_int32, _vp, _c_int32, _c_float, ctypes.c_int,
+                                            _vp, _vp, _c_int64, _vp, ctypes.c_size_t, _vp]),
+    "usp_ulysses_attn_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_int64, _vp, _c_int32,
+                                            _c_int64, _c_int32, _c_int32, _c_int32, _c_int32, _vp,
+                                            _c_int32, _c_float, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                            ctypes.c_size_t, _vp]),
 }
 
 _lib = None
@@ -217,6 +224,64 @@ def blockattn_bwd(q, k, v, o, lse, dout, position_ids=None, q_start=0, k_start=0
     return dq, dk, dv
 
 
+# ---- Ulysses attention on the sequence-sharded layout (re-layout fused) -----------
+
+def ulysses_attn_fwd(xq, xk, xv, group, position_ids=None, causal=True, scale=None, o_seq=None,
+                     lse=None, workspace=None, stream=None):
+    """xq [P][S_l][Hq][D], xk, xv [P][S_l][Hkv][D]: rank `group`'s share of the attention,
+    read in place.  Writes rank `group`'s heads of o_seq (laid out like xq; allocated
+    zero-filled if None) and returns (o_seq, lse [Hq/P][P*S_l])."""
+    import torch
+    lib = load()
+    for t, n in ((xq, "xq"), (xk, "xk"), (xv, "xv")):
+        _need(t, n)
+    P, S_l, Hq, D = xq.shape
+    Hkv = xk.shape[2]
+    S = P * S_l
+    scale = D ** -0.5 if scale is None else float(scale)
+    if o_seq is None:
+        o_seq = torch.zeros_like(xq)
+    if lse is None:
+        lse = torch.empty((Hq // P, S), dtype=torch.float32, device=xq.device)
+    _need(o_seq, "o_seq")
+    if workspace is None:
+        n = fwd_workspace_bytes(S, S, Hq // P, Hkv // P, D, _dtype_code(xq))
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=xq.device)
+    _check("usp_ulysses_attn_fwd",
+           lib.usp_ulysses_attn_fwd(_ptr(xq), _ptr(xk), _ptr(xv), P, S_l, Hq, Hkv, D, group,
+                                    _ptr(position_ids), int(bool(causal)), scale, _dtype_code(xq),
+                                    _ptr(o_seq), _ptr(lse), lse.stride(0), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o_seq, lse
+
+
+def ulysses_attn_bwd(xq, xk, xv, o_seq, lse, xdo, group, position_ids=None, causal=True, scale=None,
+                     dxq=None, dxk=None, dxv=None, workspace=None, stream=None):
+    """Gradients of ulysses_attn_fwd for rank `group`'s heads, written into that head
+    slice of dxq, dxk, dxv (sequence-sharded layouts; allocated zero-filled if None)."""
+    import torch
+    lib = load()
+    for t, n in ((xq, "xq"), (xk, "xk"), (xv, "xv"), (o_seq, "o_seq"), (xdo, "xdo")):
+        _need(t, n)
+    P, S_l, Hq, D = xq.shape
+    Hkv = xk.shape[2]
+    S = P * S_l
+    scale = D ** -0.5 if scale is None else float(scale)
+    dxq = torch.zeros_like(xq) if dxq is None else dxq
+    dxk = torch.zeros_like(xk) if dxk is None else dxk
+    dxv = torch.zeros_like(xv) if dxv is None else dxv
+    if workspace is None:
+        n = bwd_workspace_bytes(S, S, Hq // P, Hkv // P, D)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=xq.device)
+    _check("usp_ulysses_attn_bwd",
+           lib.usp_ulysses_attn_bwd(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(o_seq), _ptr(lse),
+                                    lse.stride(0), _ptr(xdo), P, S_l, Hq, Hkv, D, group,
+                                    _ptr(position_ids), int(bool(causal)), scale, _dtype_code(xq),
+                                    _ptr(dxq), _ptr(dxk), _ptr(dxv), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dxq, dxk, dxv
+
+
 def lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
     """In place: (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_part, lse_part))."""
     lib = load()
@@ -231,4 +296,5 @@ def lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
 
 
 __all__ = ["load", "seq_to_head", "head_to_seq", "blockattn_fwd", "blockattn_bwd",
+           "ulysses_attn_fwd", "ulysses_attn_bwd",
            "fwd_workspace_bytes", "bwd_workspace_bytes", "lse_merge", "UspError", "BF16", "F32", "SIGNATURES"]

@@ -74,8 +74,9 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
   if (rid >= (int64_t)f.Sq * f.Hq) return;
   const int row = (int)(rid / f.Hq);
   const int h = (int)(rid - (int64_t)row * f.Hq);
-  const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(f.o) + rid * HD + sub * 8);
-  const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.dout) + rid * HD + sub * 8);
+  const int64_t off = rows_off(f.lq, row, h) + sub * 8;
+  const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(f.o) + off);
+  const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.dout) + off);
   float acc = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc += (float)o8[j] * (float)d8[j];
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   // K and V fragments of this lane's key (B operands of S and dP): d = 16kk + 8hi + 0..7
   bf16x8 kf[8], vf[8];
   {
-    const int64_t off = ((int64_t)(key_ok ? kl : 0) * f.Hkv + hk) * HD + 8 * hi;
+    const int64_t off = rows_off(f.lk, key_ok ? kl : 0, hk) + 8 * hi;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       bf16x8 z = {};
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   const uint32_t rq_lc = (uint32_t)((((lane & 15) ^ swz16(rq_row)) << 3) * 2);
   const int rt_d = 8 * wave + (lane >> 3);
   const uint32_t rt_off = (uint32_t)((rt_d * a.sq_pad + (((lane & 7) ^ swz8(rt_d)) << 3)) * 2);
-  const uint32_t rowqB = (uint32_t)f.Hq * HD * 2;                 // bytes per q / dout row
+  const uint32_t rowqB = (uint32_t)f.lq.row_stride * 2;           // bytes per q / dout row
   const uint32_t stage_lds = lds_addr(&stage[0][0]);
 
   // DMA j (0..15) of item (h, q0) into buffer buf: load i = j/4 of tile u = j%4.
@@ -195,8 +196,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
         const uint32_t lim = (uint32_t)(f.Sq - 1 - q0);
         vq = min(rq_row + 16 * i, lim) * rowqB + rq_lc;
       }
-      const char* base = reinterpret_cast<const char*>(u == 0 ? f.q : a.dout) +
-                         ((int64_t)q0 * f.Hq + h) * HD * 2;
+      const char* base = reinterpret_cast<const char*>(u == 0 ? f.q : a.dout) + rows_off(f.lq, q0, h) * 2;
       dma16(base, vq, __builtin_amdgcn_readfirstlane(lds));
     } else {
       const char* base = reinterpret_cast<const char*>(u == 2 ? a.qt : a.dot) +
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   // ---- dK = scale dK^T, dV = dV^T (bf16), lane: key kl, d = 32db + 8g4 + 4hi + 0..3
   if (key_ok) {
-    const int64_t base = ((int64_t)kl * f.Hkv + hk) * HD;
+    const int64_t base = rows_off(f.lk, kl, hk);
     bf16* dkp = reinterpret_cast<bf16*>(a.dk) + base;
     bf16* dvp = reinterpret_cast<bf16*>(a.dv) + base;
 #pragma unroll
@@ -476,12 +476,12 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   if (rows > 0) {
     hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0,
                        stream, a);
-    hipError_t e = launch_transpose_perm16(f.q, f.Sq, f.Hq, a.qt, stream);
-    if (e == hipSuccess) e = launch_transpose_perm16(a.dout, f.Sq, f.Hq, a.dot, stream);
+    hipError_t e = launch_transpose_perm16(f.q, f.lq, f.Sq, f.Hq, a.qt, stream);
+    if (e == hipSuccess) e = launch_transpose_perm16(a.dout, f.lq, f.Sq, f.Hq, a.dot, stream);
     if (e != hipSuccess) return e;
   }
   if (f.Sk > 0) {
-    hipError_t e = launch_transpose_perm16(f.k, f.Sk, f.Hkv, a.kt, stream);
+    hipError_t e = launch_transpose_perm16(f.k, f.lk, f.Sk, f.Hkv, a.kt, stream);
     if (e != hipSuccess) return e;
     const int n_ktiles = (f.Sk + BKV - 1) / BKV;
     const int n_qtiles = (f.Sq + BQ - 1) / BQ;

@@ -77,15 +77,16 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   for (int w = 1; w < NW; ++w) { g_lo = min(g_lo, red[w][0]); g_hiex = max(g_hiex, red[w][1]); }
   g_lo = __builtin_amdgcn_readfirstlane(g_lo);
   g_hiex = __builtin_amdgcn_readfirstlane(g_hiex);
-  // local key range [kb, ke); tiles start on 16-key groups (the K^T slot order)
+  // local key range [kb, ke); tiles start on 64-key boundaries (inside one block of
+  // the key layout, and on the 16-key groups of the K^T slot order)
   const int ke = min(g_hiex, f.k_start + f.Sk) - f.k_start;
-  const int kb = (max(g_lo, f.k_start) - f.k_start) & ~15;
+  const int kb = (max(g_lo, f.k_start) - f.k_start) & ~(BC - 1);
 
   // ---- Q and dO fragments (B operands of S^T = K Q^T, dP^T = V dO^T):
   // row r32, d = 16 kk + 8 hi + 0..7 ------------------------------------------------
   bf16x8 qf[8], df[8];
   {
-    const int64_t off = ((int64_t)(row_ok ? row : 0) * f.Hq + h) * HD + 8 * hi;
+    const int64_t off = rows_off(f.lq, row_ok ? row : 0, h) + 8 * hi;
     const bf16* qsrc = reinterpret_cast<const bf16*>(f.q) + off;
     const bf16* dsrc = reinterpret_cast<const bf16*>(a.dout) + off;
 #pragma unroll
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   // The swizzle depends on the row modulo 16 only, so one lane offset serves both loads.
   const uint32_t kr0 = (uint32_t)(4 * wave + (lane >> 4));
   const uint32_t k_lc = (uint32_t)((((lane & 15) ^ swz16(kr0)) << 3) * 2);
-  const uint32_t rowkB = (uint32_t)f.Hkv * HD * 2;                // bytes per k / v row
+  const uint32_t rowkB = (uint32_t)f.lk.row_stride * 2;          // bytes per k / v row
   const int td0 = 8 * wave + (lane >> 3);
   const uint32_t t_off = (uint32_t)((td0 * a.sk_pad + (((lane & 7) ^ swz8(td0)) << 3)) * 2);
   const uint32_t stage_lds = lds_addr(&stage[0][0]);
@@ -123,8 +124,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
     if (u < 2) {   // keys past Sk are clamped to the last key (the mask zeroes them)
       const uint32_t lim = (uint32_t)(f.Sk - 1 - kt);
       const uint32_t voff = min(kr0 + 32 * i, lim) * rowkB + k_lc;
-      const char* base = reinterpret_cast<const char*>(u == 0 ? f.k : f.v) +
-                         ((int64_t)kt * f.Hkv + hk) * HD * 2;
+      const char* base = reinterpret_cast<const char*>(u == 0 ? f.k : f.v) + rows_off(f.lk, kt, hk) * 2;
       dma16(base, voff, lds);
     } else {
       const char* base = reinterpret_cast<const char*>(a.kt) +
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
 
   // ---- epilogue: dQ = scale dQ^T (bf16); lane: row r32, d = 32 db + 8 g4 + 4 hi + 0..3
   if (row_ok) {
-    bf16* dqp = reinterpret_cast<bf16*>(a.dq) + ((int64_t)row * f.Hq + h) * HD;
+    bf16* dqp = reinterpret_cast<bf16*>(a.dq) + rows_off(f.lq, row, h);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll

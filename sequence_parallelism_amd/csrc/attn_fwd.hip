@@ -98,14 +98,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   for (int w = 1; w < NW; ++w) { g_lo = min(g_lo, red[w][0]); g_hiex = max(g_hiex, red[w][1]); }
   g_lo = __builtin_amdgcn_readfirstlane(g_lo);
   g_hiex = __builtin_amdgcn_readfirstlane(g_hiex);
-  // local key range [kb, ke); tiles start on 16-key groups (the V^T slot order)
+  // local key range [kb, ke); tiles start on 64-key boundaries (inside one block of
+  // the key layout, and on the 16-key groups of the V^T slot order)
   const int ke = min(g_hiex, a.k_start + a.Sk) - a.k_start;
-  const int kb = (max(g_lo, a.k_start) - a.k_start) & ~15;
+  const int kb = (max(g_lo, a.k_start) - a.k_start) & ~(BC - 1);
 
   // ---- Q fragment (B operand of S^T = K Q^T): row r32, d = 16*kk + 8*hi + 0..7
   bf16x8 qf[8];
   {
-    const bf16* src = qp + ((int64_t)(row_ok ? row : 0) * a.Hq + h) * HD + 8 * hi;
+    const bf16* src = qp + rows_off(a.lq, row_ok ? row : 0, h) + 8 * hi;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       bf16x8 z = {};
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   // The swizzle depends on the row modulo 16 only, so one lane offset serves both loads.
   const uint32_t kr0 = (uint32_t)(4 * wave + (lane >> 4));
   const uint32_t k_lc = (uint32_t)((((lane & 15) ^ swz16(kr0)) << 3) * 2);
-  const uint32_t rowkB = (uint32_t)a.Hkv * HD * 2;                // bytes per k row
+  const uint32_t rowkB = (uint32_t)a.lk.row_stride * 2;          // bytes per k row
   const int td0 = 8 * wave + (lane >> 3);
   const uint32_t t_off = (uint32_t)((td0 * a.vt_ld + (((lane & 7) ^ swz8(td0)) << 3)) * 2);
   const uint32_t stage_lds = lds_addr(&stage[0][0]);
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
     if (u == 0) {   // keys past Sk are clamped to the last key (the mask zeroes them)
       const uint32_t lim = (uint32_t)(a.Sk - 1 - kt);
       const uint32_t voff = min(kr0 + 32 * i, lim) * rowkB + k_lc;
-      dma16(reinterpret_cast<const char*>(a.k) + ((int64_t)kt * a.Hkv + hk) * HD * 2, voff, lds);
+      dma16(reinterpret_cast<const char*>(a.k) + rows_off(a.lk, kt, hk) * 2, voff, lds);
     } else {        // the padded copy covers every position of the tile
       dma16(reinterpret_cast<const char*>(a.vt) + (((int64_t)hk * HD + 64 * i) * a.vt_ld + kt) * 2,
             t_off, lds);
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_ok) {
-    const int64_t obase = ((int64_t)row * a.Hq + h) * HD;
+    const int64_t obase = rows_off(a.lq, row, h);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -343,7 +344,7 @@ void attn_fwd_workspace_layout(AttnArgs& a, void* base) {
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t stream) {
   if (a.Sq == 0) return hipSuccess;
   if (a.Sk > 0) {
-    hipError_t e = launch_transpose_perm16(a.v, a.Sk, a.Hkv, const_cast<void*>(a.vt), stream);
+    hipError_t e = launch_transpose_perm16(a.v, a.lk, a.Sk, a.Hkv, const_cast<void*>(a.vt), stream);
     if (e != hipSuccess) return e;
   }
   const int n_qtiles = (a.Sq + BR - 1) / BR;

@@ -31,6 +31,39 @@ struct PermuteArgs {
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 
+// Where token `row`, head `h` of a token-major tensor starts (elements; head dim 128
+// on the MFMA paths): block b = row / blk_rows, then
+//   b * blk_stride + (row - b * blk_rows) * row_stride + (head0 + h) * 128.
+// Contiguous [S][H][128]: row_stride = 128 H and blk_stride = blk_rows * row_stride,
+// so the block split is immaterial.  The sequence-sharded Ulysses layout
+// [P][S_l][H_total][128] read for rank g's heads: row_stride = 128 H_total,
+// blk_rows = S_l, blk_stride = S_l * 128 H_total, head0 = g H_total / P.  The MFMA
+// kernels keep every tile inside one block, so blk_rows is then a multiple of 256.
+// The division by blk_rows (>= 2) is a multiply-high by a magic number made on the host.
+struct RowLayout {
+  int64_t row_stride;
+  int64_t blk_stride;
+  int32_t blk_rows;
+  int32_t head0;
+  uint32_t div_m, div_s;
+};
+inline RowLayout make_rows(int64_t row_stride, int32_t blk_rows, int64_t blk_stride, int32_t head0) {
+  uint32_t l = 0;
+  while ((1ull << l) < (uint64_t)blk_rows) ++l;
+  const uint32_t m = (uint32_t)(((1ull << 32) * ((1ull << l) - (uint64_t)blk_rows)) / (uint64_t)blk_rows + 1);
+  return RowLayout{row_stride, blk_stride, blk_rows, head0, m, l};
+}
+inline RowLayout contiguous_rows(int32_t H) {
+  return make_rows((int64_t)H * 128, 1 << 30, ((int64_t)1 << 30) * H * 128, 0);
+}
+__device__ __forceinline__ int64_t rows_off(const RowLayout& L, int row, int h) {
+  const uint32_t n = (uint32_t)row;
+  const uint32_t t = __umulhi(n, L.div_m);
+  const int b = (int)((t + ((n - t) >> 1)) >> (L.div_s - 1));
+  return (int64_t)b * L.blk_stride + (int64_t)(row - b * L.blk_rows) * L.row_stride +
+         (int64_t)(L.head0 + h) * 128;
+}
+
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -46,6 +79,8 @@ struct AttnArgs {
   const void* vt;      // bf16 path: V in head-dim-major layout (see transpose.hip)
   int64_t vt_ld;       // its padded token length
   int* q_order;        // bf16 path: query tiles heaviest first (schedule.hip)
+  RowLayout lq;        // bf16 path: rows of q, o (and of dout, dq in the backward)
+  RowLayout lk;        // bf16 path: rows of k, v (and of dk, dv)
 };
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t s);
 size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hkv, int32_t D, int bf16_path);
@@ -87,7 +122,8 @@ hipError_t launch_schedule_q_tiles(const AttnArgs& a, int n_tiles, int br, int* 
 // Y[h][d][p] = X[tok(p)][h][d] over a padded token axis, 16-token groups permuted
 // to MFMA slot order (transpose.hip); D = 128, bf16.
 int64_t transpose_perm16_padded_len(int64_t S);
-hipError_t launch_transpose_perm16(const void* x, int64_t S, int32_t H, void* y, hipStream_t s);
+hipError_t launch_transpose_perm16(const void* x, const RowLayout& lx, int64_t S, int32_t H, void* y,
+                                   hipStream_t s);
 
 struct MergeArgs {
   void* o_acc;

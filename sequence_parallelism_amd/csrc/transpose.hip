@@ -1,4 +1,5 @@
-// Head-dim-major copy of a [S][H][128] bf16 tensor, used to feed MFMA operands
+// Head-dim-major copy of a token-major [S][H][128] bf16 tensor (rows placed by a
+// RowLayout, so it also reads one rank's heads of the sequence-sharded layout), used to feed MFMA operands
 // whose reduction index is the token: Y[h][d][p] = X[tok(p)][h][d] over a padded
 // token axis of length Spad.  Inside every aligned group of 16 tokens the order is
 // permuted so that a lane's eight reduction slots of a 32x32x16 MFMA (tokens
@@ -17,8 +18,8 @@ constexpr int HD = 128;
 constexpr int TT = 64;              // tokens per tile
 constexpr int T_LD = HD + 2;        // LDS row pitch (bf16), spreads the 2-byte column reads
 
-__global__ __launch_bounds__(256) void transpose_perm16_kernel(const bf16* __restrict__ x, int64_t S,
-                                                               int32_t H, bf16* __restrict__ y,
+__global__ __launch_bounds__(256) void transpose_perm16_kernel(const bf16* __restrict__ x, RowLayout lx,
+                                                               int64_t S, bf16* __restrict__ y,
                                                                int64_t Spad) {
   __shared__ bf16 T[TT * T_LD];
   const int tid = threadIdx.x;
@@ -30,7 +31,7 @@ __global__ __launch_bounds__(256) void transpose_perm16_kernel(const bf16* __res
     const int c = tid + 256 * u;
     const int r = c >> 4, ch = c & 15;
     bf16x8 v = {};
-    if (t0 + r < S) v = *reinterpret_cast<const bf16x8*>(x + ((t0 + r) * H + h) * HD + ch * 8);
+    if (t0 + r < S) v = *reinterpret_cast<const bf16x8*>(x + rows_off(lx, (int)(t0 + r), h) + ch * 8);
 #pragma unroll
     for (int j = 0; j < 8; ++j) T[r * T_LD + ch * 8 + j] = v[j];
   }
@@ -53,10 +54,11 @@ __global__ __launch_bounds__(256) void transpose_perm16_kernel(const bf16* __res
 
 int64_t transpose_perm16_padded_len(int64_t S) { return ((S + TT - 1) / TT) * TT + TT; }
 
-hipError_t launch_transpose_perm16(const void* x, int64_t S, int32_t H, void* y, hipStream_t stream) {
+hipError_t launch_transpose_perm16(const void* x, const RowLayout& lx, int64_t S, int32_t H, void* y,
+                                   hipStream_t stream) {
   const int64_t Spad = transpose_perm16_padded_len(S);
   dim3 grid((unsigned)(Spad / TT), (unsigned)H);
   hipLaunchKernelGGL(transpose_perm16_kernel, grid, dim3(256), 0, stream,
-                     reinterpret_cast<const bf16*>(x), S, H, reinterpret_cast<bf16*>(y), Spad);
+                     reinterpret_cast<const bf16*>(x), lx, S, reinterpret_cast<bf16*>(y), Spad);
   return hipGetLastError();
 }

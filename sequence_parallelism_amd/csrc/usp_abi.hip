@@ -66,6 +66,8 @@ AttnArgs make_args(const void* q, const void* k, const void* v, int64_t Sq, int6
   a.vt = nullptr;
   a.vt_ld = 0;
   a.q_order = nullptr;
+  a.lq = contiguous_rows(Hq);
+  a.lk = contiguous_rows(Hkv);
   return a;
 }
 
@@ -191,6 +193,91 @@ usp_status lse_merge(void* o_acc, usp_dtype acc_dtype, float* lse_acc, int64_t l
   a.S = S; a.H = H; a.D = D;
   a.acc_f32 = acc_dtype == USP_F32; a.part_f32 = part_dtype == USP_F32;
   return hip_status(launch_lse_merge(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---- Ulysses attention reading the sequence-sharded layout directly ---------------
+
+namespace {
+
+// Validates the sharded-layout arguments and fills the attention arguments of rank
+// `group`'s share (Sq = Sk = P S_local, its Hq_total/P query and Hkv_total/P key/value
+// heads), with row layouts that address [P][S_local][H_total][D] directly.
+usp_status ulysses_args(const void* xq, const void* xk, const void* xv, int32_t P, int64_t S_local,
+                        int32_t Hq_total, int32_t Hkv_total, int32_t D, int32_t group,
+                        const int32_t* pos, int32_t causal, float scale, usp_dtype in_dt, void* o,
+                        const float* lse, int64_t lse_ld, AttnArgs* out) {
+  if (!xq || !xk || !xv || !o || !lse || (causal && !pos)) return USP_ERR_NULL_POINTER;
+  if (bad_dtype(in_dt)) return USP_ERR_BAD_DTYPE;
+  if (in_dt != USP_BF16 || D != 128) return USP_ERR_UNSUPPORTED;
+  if (P < 1 || S_local < 1 || Hq_total < 1 || Hkv_total < 1 || group < 0 || group >= P)
+    return USP_ERR_BAD_SHAPE;
+  if (Hq_total % P || Hkv_total % P || (Hq_total / P) % (Hkv_total / P)) return USP_ERR_NOT_DIVISIBLE;
+  const int64_t S = (int64_t)P * S_local;
+  if (lse_ld < S) return USP_ERR_BAD_SHAPE;
+  // every MFMA tile (up to 256 rows) stays inside one shard; indices are 32-bit
+  if (S_local % 256 || S > I32_MAX || S * Hq_total > I32_MAX) return USP_ERR_UNSUPPORTED;
+  if (!(aligned(xq, 16) && aligned(xk, 16) && aligned(xv, 16) && aligned(o, 16) && aligned(lse, 4) &&
+        (!pos || aligned(pos, 4))))
+    return USP_ERR_MISALIGNED;
+  const int32_t hq = Hq_total / P, hkv = Hkv_total / P;
+  AttnArgs a = make_args(xq, xk, xv, S, S, hq, hkv, D, pos, 0, 0, causal, scale, o,
+                         const_cast<float*>(lse), lse_ld);
+  a.lq = make_rows((int64_t)Hq_total * D, (int32_t)S_local, S_local * Hq_total * (int64_t)D, group * hq);
+  a.lk = make_rows((int64_t)Hkv_total * D, (int32_t)S_local, S_local * Hkv_total * (int64_t)D,
+                   group * hkv);
+  *out = a;
+  return USP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+usp_status usp_ulysses_attn_fwd(const void* xq, const void* xk, const void* xv, int32_t P,
+                                int64_t S_local, int32_t Hq_total, int32_t Hkv_total, int32_t D,
+                                int32_t group, const int32_t* position_ids, int32_t causal,
+                                float softmax_scale, usp_dtype in_dtype, void* o_seq, float* lse,
+                                int64_t lse_ld, void* workspace, size_t workspace_bytes, void* stream) {
+  AttnArgs a;
+  usp_status st = ulysses_args(xq, xk, xv, P, S_local, Hq_total, Hkv_total, D, group, position_ids,
+                               causal, softmax_scale, in_dtype, o_seq, lse, lse_ld, &a);
+  if (st != USP_OK) return st;
+  const size_t need = attn_fwd_workspace_bytes(a.Sq, a.Sk, a.Hkv, D, 1);
+  if (!workspace) return USP_ERR_NULL_POINTER;
+  if (!aligned(workspace, 16)) return USP_ERR_MISALIGNED;
+  if (workspace_bytes < need) return USP_ERR_WORKSPACE_TOO_SMALL;
+  attn_fwd_workspace_layout(a, workspace);
+  return hip_status(launch_attn_fwd_bf16(a, 0, reinterpret_cast<hipStream_t>(stream)));
+}
+
+usp_status usp_ulysses_attn_bwd(const void* xq, const void* xk, const void* xv, const void* o_seq,
+                                const float* lse, int64_t lse_ld, const void* xdo, int32_t P,
+                                int64_t S_local, int32_t Hq_total, int32_t Hkv_total, int32_t D,
+                                int32_t group, const int32_t* position_ids, int32_t causal,
+                                float softmax_scale, usp_dtype in_dtype, void* dxq, void* dxk,
+                                void* dxv, void* workspace, size_t workspace_bytes, void* stream) {
+  AttnArgs f;
+  usp_status st = ulysses_args(xq, xk, xv, P, S_local, Hq_total, Hkv_total, D, group, position_ids,
+                               causal, softmax_scale, in_dtype, const_cast<void*>(o_seq), lse, lse_ld,
+                               &f);
+  if (st != USP_OK) return st;
+  if (!xdo || !dxq || !dxk || !dxv || !workspace) return USP_ERR_NULL_POINTER;
+  if (!(aligned(xdo, 16) && aligned(dxq, 16) && aligned(dxk, 16) && aligned(dxv, 16) &&
+        aligned(workspace, 256)))
+    return USP_ERR_MISALIGNED;
+  if (!attn_bwd_supported(f.Sq, f.Sk, Hq_total, Hkv_total)) return USP_ERR_UNSUPPORTED;
+  if (workspace_bytes < attn_bwd_workspace_bytes(f.Sq, f.Sk, f.Hq, f.Hkv, D))
+    return USP_ERR_WORKSPACE_TOO_SMALL;
+  AttnBwdArgs a;
+  a.f = f;
+  a.dout = xdo;
+  a.dq = dxq;
+  a.dk = dxk;
+  a.dv = dxv;
+  attn_bwd_workspace_layout(a, workspace);
+  return hip_status(launch_attn_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

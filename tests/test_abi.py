@@ -29,10 +29,10 @@ def lib():
     return usp.load()
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("usp_seq_to_head_permute", "usp_head_to_seq_permute", "blockattn_fwd",
-              "blockattn_bwd", "lse_merge"):
+              "blockattn_bwd", "lse_merge", "usp_ulysses_attn_fwd", "usp_ulysses_attn_bwd"):
         assert n in names
 
 
@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.usp_abi_version() == 1
+    assert lib.usp_abi_version() == 2
     for code in range(9):
         s = lib.usp_status_string(code).decode()
         assert s and s != "unknown status"
@@ -128,3 +128,36 @@ def test_merge_validation(lib):
     assert m(lda=8) == SHAPE
     assert m(H=0) == SHAPE
     assert m(oa=A + 2) == MISAL
+
+
+def test_ulysses_fused_validation(lib):
+    """Sequence-sharded entry points: the same argument checks, plus the shard-size
+    and head-divisibility rules of the fused layout."""
+    n = ctypes.c_size_t(1 << 30)
+
+    def fwd(xq=A, P=8, S_l=256, Hq=32, Hkv=8, D=128, g=0, pos=A, dt=0, o=A, lse=A, ld=2048,
+            ws=A, wsb=n.value):
+        return lib.usp_ulysses_attn_fwd(xq, A, A, P, S_l, Hq, Hkv, D, g, pos, 1, 0.1, dt, o, lse, ld,
+                                        ws, wsb, None)
+    assert fwd(xq=None) == NULLP
+    assert fwd(pos=None) == NULLP
+    assert fwd(ws=None) == NULLP
+    assert fwd(dt=1) == UNSUP
+    assert fwd(D=64) == UNSUP
+    assert fwd(S_l=200) == UNSUP          # tiles must stay inside one shard
+    assert fwd(g=8) == SHAPE
+    assert fwd(P=0) == SHAPE
+    assert fwd(Hq=30) == NOTDIV
+    assert fwd(Hq=8, Hkv=16) == NOTDIV    # 1 query head per rank, 2 key/value heads
+    assert fwd(ld=2047) == SHAPE
+    assert fwd(xq=A + 8) == MISAL
+    assert fwd(wsb=16) == WS
+
+    def bwd(xdo=A, dxq=A, ws=A, wsb=n.value, S_l=256):
+        return lib.usp_ulysses_attn_bwd(A, A, A, A, A, 2048, xdo, 8, S_l, 32, 8, 128, 0, A, 1, 0.1, 0,
+                                        dxq, A, A, ws, wsb, None)
+    assert bwd(xdo=None) == NULLP
+    assert bwd(dxq=None) == NULLP
+    assert bwd(ws=A + 16) == MISAL
+    assert bwd(wsb=16) == WS
+    assert bwd(S_l=128) == UNSUP
