@@ -125,6 +125,10 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
       kf[kk] = key_ok ? *reinterpret_cast<const bf16x8*>(kp + off + 16 * kk) : z;
       vf[kk] = key_ok ? *reinterpret_cast<const bf16x8*>(vp + off + 16 * kk) : z;
     }
+    // consumed here, so that the compiler waits for these loads once, now, and not
+    // inside the item loop (where its wait would also cover the tile DMA in flight)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) asm volatile("" :: "v"(kf[kk]), "v"(vf[kk]));
   }
   // ---- per-lane LDS offsets, swizzled ------------------------------------------------
   // Logical chunk 2k + hi of row r sits at physical chunk (2k + hi) ^ swz(r) = 2k ^ t
@@ -256,6 +260,27 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) { dka[i] = f32x16{}; dva[i] = f32x16{}; }
 
+  // LDS operand of MFMA i of the item staged in buffer b
+  auto op_at = [&](auto I, int b) {
+    constexpr int i = decltype(I)::v, slot = i / 16, j = i % 16;
+    if constexpr (slot < 2) {   // S or dP of block qb = slot, k-step kk (sdp_order)
+      constexpr int dp = sdp_order(j) >> 3, kk = sdp_order(j) & 7;
+      const bf16* t = &stage[b][(dp ? 1 : 0) * TILE];
+      return *reinterpret_cast<const bf16x8*>(&t[32 * slot * HD + (qbase ^ (16 * kk))]);
+    } else {                    // dV^T (even) / dK^T (odd), row chunk c, head-dim block db
+      constexpr int c = 2 * (slot - 2) + (j >> 3), db = (j >> 1) & 3;
+      const bf16* t = &stage[b][((j & 1) ? 2 : 3) * TILE];
+      return *reinterpret_cast<const bf16x8*>(&t[32 * db * BQ + (tbase ^ (16 * c))]);
+    }
+  };
+  // -D of rows 32qb + 8g4 + 4hi + 0..3 (the dP accumulators' start), from buffer b
+  f32x4 e4[2][4];
+  auto load_nd = [&](auto QB, auto G4, int b) {
+    constexpr int qb = decltype(QB)::v, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
+    e4[qb][g4] = *reinterpret_cast<const f32x4*>(&ndelta_s[b][q + 4 * hi]);
+  };
+  bf16x8 ops[PF];   // operand reads in flight, carried from item to item
+
   // (h, tc): the current item; (hn, tn): the next one (the last item repeats itself)
   int h = hk * grp, tc = n_full > 0 ? f0 : first_masked;
   int hn = h, tn = tc;
@@ -266,6 +291,9 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
     load_scalars(h, tc * BQ);
     wait_vmem();
     store_scalars(0);
+    __syncthreads();
+    unroll<PF>([&](auto I) { ops[decltype(I)::v] = op_at(I, 0); });
+    unroll<4>([&](auto G4) { load_nd(IC<0>{}, G4, 0); });
   }
 
   // one item; MASK: a boundary item, whose hidden (row, key) pairs get the row
@@ -273,16 +301,13 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   auto run_item = [&](auto mask_tag, int it) {
     constexpr bool MASK = decltype(mask_tag)::v != 0;
     const int buf = it & 1;
-    const int q0 = tc * BQ, q0n = tn * BQ;
-    __syncthreads();   // item `it` staged with its row scalars; buffer buf ^ 1 free
-
-    const bf16* Qb = &stage[buf][0 * TILE];
-    const bf16* Db = &stage[buf][1 * TILE];
-    const bf16* Qtb = &stage[buf][2 * TILE];
-    const bf16* Dtb = &stage[buf][3 * TILE];
+    const int q0n = tn * BQ;
+    // every wave is done with item it-1, which read buffer buf ^ 1: it can be refilled
+    // (item it itself was published halfway through item it-1's last slot)
+    __syncthreads();
     {
       f32x16 sacc[2], dpacc[2];
-      f32x4 l4[2][4], e4[2][4];
+      f32x4 l4[2][4];
       bf16x8 pb[2][2], sb[2][2];
       uint32_t vq = 0;
 
@@ -308,10 +333,6 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
         }
       };
       // row scalars of rows 32qb + 8g4 + 4hi + 0..3, read four steps before first use
-      auto load_nd = [&](auto QB, auto G4) {   // -D of the same rows
-        constexpr int qb = decltype(QB)::v, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
-        e4[qb][g4] = *reinterpret_cast<const f32x4*>(&ndelta_s[buf][q + 4 * hi]);
-      };
       auto load_rows = [&](auto QB, auto G4) {
         constexpr int qb = decltype(QB)::v, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
         l4[qb][g4] = *reinterpret_cast<const f32x4*>(&lse2_s[buf][q + 4 * hi]);
@@ -327,19 +348,12 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
           }
         }
       };
-      unroll<4>([&](auto G4) { load_nd(IC<0>{}, G4); });   // needed by block 0's first dP
-      mfma_pipeline<PF, 64>(
-          [&](auto I) {   // LDS operand of MFMA i
-            constexpr int i = decltype(I)::v, slot = i / 16, j = i % 16;
-            if constexpr (slot < 2) {   // S or dP of block qb = slot, k-step kk (sdp_order)
-              constexpr int dp = sdp_order(j) >> 3, kk = sdp_order(j) & 7;
-              const bf16* t = dp ? Db : Qb;
-              return *reinterpret_cast<const bf16x8*>(&t[32 * slot * HD + (qbase ^ (16 * kk))]);
-            } else {                    // dV^T (even) / dK^T (odd), row chunk c, head-dim block db
-              constexpr int c = 2 * (slot - 2) + (j >> 3), db = (j >> 1) & 3;
-              const bf16* t = (j & 1) ? Qtb : Dtb;
-              return *reinterpret_cast<const bf16x8*>(&t[32 * db * BQ + (tbase ^ (16 * c))]);
-            }
+      mfma_pipeline_carry<PF, 64>(
+          ops,
+          [&](auto I) {   // LDS operand of MFMA i; past the item, the next item's first ones
+            constexpr int i = decltype(I)::v;
+            if constexpr (i < 64) return op_at(I, buf);
+            else return op_at(IC<i - 64>{}, buf ^ 1);
           },
           [&](auto I, const bf16x8& op) {
             constexpr int i = decltype(I)::v, slot = i / 16, j = i % 16;
@@ -373,9 +387,19 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
               constexpr int qb = i < 28 ? 0 : 1, g4 = (i - 12 - 16 * qb) / 4;
               load_rows(IC<qb>{}, IC<g4>{});
             }
-            if constexpr (i >= 8 && i < 12) load_nd(IC<1>{}, IC<i - 8>{});
-            if constexpr (i % 3 == 1 && i < 48) dma_step(i / 3, hn, q0n, buf ^ 1, vq);   // item it+1
+            if constexpr (i >= 8 && i < 12) load_nd(IC<1>{}, IC<i - 8>{}, buf);
+            if constexpr (i % 2 == 1 && i < 32) dma_step(i / 2, hn, q0n, buf ^ 1, vq);   // item it+1
             if constexpr (i == 2) load_scalars(hn, q0n);                           // its row scalars
+            if constexpr (i == 56) {
+              // item it+1 has landed (its DMA was issued in the first half of this item),
+              // and so have its row scalars, which go to the other buffer; the barrier
+              // publishes both, and the reads for item it+1's first MFMAs and its -D
+              // start behind this item's last eight
+              wait_vmem();
+              store_scalars(buf ^ 1);
+              __syncthreads();
+            }
+            if constexpr (i >= 57 && i < 61) load_nd(IC<0>{}, IC<i - 57>{}, buf ^ 1);
             // block 0's softmax behind block 1's S, dP; block 1's behind block 0's dV, dK
             if constexpr (slot == 1) {
               soft_a(IC<0>{}, IC<j>{});
@@ -390,10 +414,6 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
           });
     }
 
-    // item it+1 has landed (its DMA was issued a whole item ago), and so have its row
-    // scalars, which go to the other buffer (published by the next item's barrier)
-    wait_vmem();
-    store_scalars(buf ^ 1);
     h = hn; tc = tn;
     if (it + 2 < n_items) next_item(hn, tn);
   };

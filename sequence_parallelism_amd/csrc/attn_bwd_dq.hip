@@ -104,6 +104,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
     lse2 = l == -INFINITY ? INFINITY : l * USP_LOG2E;
     dlt = a.delta[(int64_t)h * f.Sq + row];
   }
+  // consumed here, so that the compiler waits for these loads once, now, and not
+  // inside the tile loop (where its wait would also cover the tile DMA in flight)
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) asm volatile("" :: "v"(qf[kk]), "v"(df[kk]));
+  asm volatile("" :: "v"(lse2), "v"(dlt));
   const float sl2 = f.scale * USP_LOG2E;
 
   // ---- staging by LDS-DMA: tile u (K, V, K^T), load i (0..1) of wave w covers
@@ -184,16 +189,16 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
     const bool full = (kt + BC <= ke) && (!f.causal || (gk0 + BC - 1 <= w_gqmin && gk0 >= w_dsmax));
     if (!full) {
       const int klim = ke - kt;
-      // visible: lo_k <= key <= hi_k (no int32 overflow: ds, gq, gk0 are in [0, 2^31))
-      const int lo_k = f.causal ? max(ds - gk0, kb - kt) : kb - kt;
-      const int hi_k = f.causal ? gq - gk0 : BC;
+      // visible: lo_k <= key <= hi_k (no int32 overflow: ds, gq, gk0 are in [0, 2^31));
+      // key = 4 hi + c with c a constant of the register, so the bounds move instead
+      const int lo_k = (f.causal ? max(ds - gk0, kb - kt) : kb - kt) - 4 * hi;
+      const int hi_k = min(f.causal ? gq - gk0 : BC, klim - 1) - 4 * hi;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = 32 * kb2 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          const bool vis = (key < klim) & (key >= lo_k) & (key <= hi_k);
-          sacc[kb2][i] = vis ? sacc[kb2][i] : -INFINITY;
+          const int c = 32 * kb2 + 8 * (i >> 2) + (i & 3);
+          sacc[kb2][i] = (c >= lo_k) & (c <= hi_k) ? sacc[kb2][i] : -INFINITY;
         }
       }
     }

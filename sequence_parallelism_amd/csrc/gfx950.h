@@ -16,9 +16,11 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // LDS tiles are unpadded; 16-byte chunk c of row r is stored at c ^ swz(r).  With
 // these, 16 lanes reading 16 consecutive rows at one logical chunk touch all 64
-// banks once.  Rows of 128 bf16 have 16 chunks, rows of 64 bf16 have 8.
+// banks once.  Rows of 128 bf16 have 16 chunks, rows of 64 bf16 have 8, rows of 32
+// bf16 have 4.
 __device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
 
 // Compile-time loop: f(IC<0>{}), f(IC<1>{}), ..., so every index is a constant.
 template <int N> struct IC { static constexpr int v = N; };
@@ -49,6 +51,23 @@ __device__ __forceinline__ void mfma_pipeline(Load&& load, Mma&& mma, Side&& sid
   });
 }
 
+// The same with the operand ring carried from call to call: on entry ops holds the
+// reads for MFMAs 0 .. PF-1 (issued by the previous call or a prologue), on exit the
+// reads load(NS) .. load(NS + PF - 1), i.e. the next call's first operands (NS must be
+// a multiple of PF).
+template <int PF, int NS, typename Load, typename Mma, typename Side>
+__device__ __forceinline__ void mfma_pipeline_carry(bf16x8 (&ops)[PF], Load&& load, Mma&& mma, Side&& side) {
+  static_assert(NS % PF == 0, "the ring must line up with the next call");
+  unroll<NS>([&](auto I) {
+    constexpr int i = decltype(I)::v;
+    const bf16x8 op = ops[i % PF];
+    ops[i % PF] = load(IC<i + PF>{});
+    mma(I, op);
+    side(I);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
 // LDS-DMA of 16 bytes per lane from sbase + voff (sbase wave-uniform): lane l's data
 // lands at LDS byte address lds + 16 l.  Issued as inline assembly so that the
 // compiler does not guard every later LDS read with a wait for it; completion is
@@ -61,6 +80,13 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+// max(x, x of the lane 32 apart), on the VALU (v_permlane32_swap: each lane ends up
+// with both values of its pair, in some order)
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ int wave_min(int x) {
