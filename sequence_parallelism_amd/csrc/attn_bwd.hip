@@ -92,8 +92,8 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   __shared__ __attribute__((aligned(16))) bf16 stage[2][4 * TILE];
   __shared__ __attribute__((aligned(16))) float lse2_s[2][BQ];
   __shared__ __attribute__((aligned(16))) float ndelta_s[2][BQ];   // -D
-  __shared__ __attribute__((aligned(16))) int dsq_s[2][BQ];
-  __shared__ __attribute__((aligned(16))) int gq_s[2][BQ];
+  __shared__ __attribute__((aligned(16))) int klo_s[2][BQ];   // visible keys [klo, khi)
+  __shared__ __attribute__((aligned(16))) int khi_s[2][BQ];
 
   const AttnArgs& f = a.f;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -106,9 +106,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   const int kw0 = k0 + wave * 32;                       // this wave's first key
   const int kl = kw0 + r32;                             // this lane's key (B-operand column)
   const bool key_ok = kl < f.Sk;
-  const int gk = f.k_start + kl;
-  const int gk_first = f.k_start + k0;
-  const int gk_last = f.k_start + min(k0 + BKV, f.Sk) - 1;
+  const int k_last = min(k0 + BKV, f.Sk) - 1;           // the block's last key
   const int grp = f.Hq / f.Hkv;
   const float sl2 = f.scale * USP_LOG2E;
 
@@ -141,29 +139,31 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
 
   // ---- query tiles that can see the block: [t0, t1) ------------------------------
   // and among them the fully visible ones [f0, f1): every row valid, every key of
-  // the block valid, and every (row, key) pair unmasked.  Rows are in order and
-  // document starts never decrease, so the causal bound needs the tile's first row
-  // at or after the block's last key, and the document bound needs the last row's
-  // document to start at or before the block's first key.
+  // the block valid, and every (row, key) pair unmasked.  A row's visible keys
+  // [lo, hiex) (row_keys) have both ends nondecreasing along the rows, so the causal
+  // bound needs the tile's first row to see the block's last key, and the document
+  // bound needs the last row's first visible key at or before the block's first.
   int t0 = 0, t1 = n_qtiles, f0 = 0, f1 = min(n_qtiles, f.Sq / BQ);
   if (f.causal) {
-    t0 = min(max(gk_first - f.q_start, 0) / BQ, n_qtiles);
-    // first tile whose first row starts its document after the block's last key
+    t0 = min(first_row_seeing(f, k0) / BQ, n_qtiles);
+    // first tile whose first row's visible keys start after the block's last key
     int lo_t = t0, hi_t = n_qtiles;
     while (lo_t < hi_t) {
       const int mid = (lo_t + hi_t) >> 1;
-      const int g = f.q_start + mid * BQ;
-      if (g - f.pos[g] > gk_last) hi_t = mid; else lo_t = mid + 1;
+      int lo_k, hiex_k;
+      row_keys(f, mid * BQ, lo_k, hiex_k);
+      if (lo_k > k_last) hi_t = mid; else lo_t = mid + 1;
     }
     t1 = lo_t;
-    f0 = max(t0, (max(gk_last - f.q_start, 0) + BQ - 1) / BQ);
-    // first complete tile whose last row starts its document after the block's first key
+    f0 = max(t0, (first_row_seeing(f, k_last) + BQ - 1) / BQ);
+    // first complete tile whose last row's visible keys start after the block's first key
     lo_t = f0;
     hi_t = max(f1, f0);
     while (lo_t < hi_t) {
       const int mid = (lo_t + hi_t) >> 1;
-      const int g = f.q_start + mid * BQ + BQ - 1;
-      if (g - f.pos[g] > gk_first) hi_t = mid; else lo_t = mid + 1;
+      int lo_k, hiex_k;
+      row_keys(f, mid * BQ + BQ - 1, lo_k, hiex_k);
+      if (lo_k > k0) hi_t = mid; else lo_t = mid + 1;
     }
     f1 = min(lo_t, t1);
   }
@@ -190,38 +190,62 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   const uint32_t rowqB = (uint32_t)f.lq.row_stride * 2;           // bytes per q / dout row
   const uint32_t stage_lds = lds_addr(&stage[0][0]);
 
-  // DMA j (0..15) of item (h, q0) into buffer buf: load i = j/4 of tile u = j%4.
-  // vq carries the clamped row offset from tile 0 to tile 1 of the same load.
-  auto dma_step = [&](int j, int h, int q0, int buf, uint32_t& vq) {
+  // Where the data of item (h, t) comes from, worked out one item before its DMA is
+  // issued (the address arithmetic, 64-bit and scalar, would otherwise sit between
+  // the first MFMAs of the item that issues it): the four tiles' sources, the row
+  // clamp, and this lane's row-scalar addresses.
+  struct ItemSrc {
+    const char* tile[4];   // Q, dO rows q0.. ; Q^T, dO^T columns q0..
+    uint32_t lim;          // rows past Sq are clamped to the last row (the mask zeroes them)
+    int q0;
+    const float* lse;
+    const float* delta;
+    const int* pos;
+  };
+  const int* const pos_or_dummy = f.causal ? f.pos : reinterpret_cast<const int*>(f.lse);
+  auto item_src = [&](int h, int t) {
+    ItemSrc r;
+    const int q0 = t * BQ;
+    const int64_t rq = rows_off(f.lq, q0, h) * 2;
+    r.tile[0] = reinterpret_cast<const char*>(f.q) + rq;
+    r.tile[1] = reinterpret_cast<const char*>(a.dout) + rq;
+    const int64_t rt = ((int64_t)h * HD * a.sq_pad + q0) * 2;
+    r.tile[2] = reinterpret_cast<const char*>(a.qt) + rt;
+    r.tile[3] = reinterpret_cast<const char*>(a.dot) + rt;
+    r.lim = (uint32_t)(f.Sq - 1 - q0);
+    r.q0 = q0;
+    const int row = min(q0 + lane, f.Sq - 1);
+    r.lse = f.lse + (int64_t)h * f.lse_ld + row;
+    r.delta = a.delta + (int64_t)h * f.Sq + row;
+    r.pos = pos_or_dummy + (f.causal ? f.q_start + f.q_stride * row : 0);
+    return r;
+  };
+
+  // DMA j (0..15) of an item into buffer buf: load i = j/4 of tile u = j%4 (the
+  // head-dim-major tiles step 32 head-dim rows per load).  vq carries the clamped row
+  // offset from tile 0 to tile 1 of the same load.
+  auto dma_step = [&](int j, const ItemSrc& src, int buf, uint32_t& vq) {
     const int i = j >> 2, u = j & 3;
     const uint32_t lds = stage_lds + (uint32_t)(((buf * 4 + u) * TILE + (4 * i + wave) * 512) * 2);
     if (u < 2) {
-      if (u == 0) {   // rows past Sq are clamped to the last row (the mask zeroes them)
-        const uint32_t lim = (uint32_t)(f.Sq - 1 - q0);
-        vq = min(rq_row + 16 * i, lim) * rowqB + rq_lc;
-      }
-      const char* base = reinterpret_cast<const char*>(u == 0 ? f.q : a.dout) + rows_off(f.lq, q0, h) * 2;
-      dma16(base, vq, __builtin_amdgcn_readfirstlane(lds));
+      if (u == 0) vq = min(rq_row + 16 * i, src.lim) * rowqB + rq_lc;
+      dma16(src.tile[u], vq, __builtin_amdgcn_readfirstlane(lds));
     } else {
-      const char* base = reinterpret_cast<const char*>(u == 2 ? a.qt : a.dot) +
-                         (((int64_t)h * HD + 32 * i) * a.sq_pad + q0) * 2;
-      dma16(base, rt_off, __builtin_amdgcn_readfirstlane(lds));
+      dma16(src.tile[u] + (int64_t)32 * i * a.sq_pad * 2, rt_off, __builtin_amdgcn_readfirstlane(lds));
     }
   };
 
   // Row scalars of an item, one row per lane, read one item ahead.  The reads are
   // issued by every wave with no arithmetic on their results (that would stall the
-  // pipeline they sit in for a whole memory latency); wave 0 finishes and stores
-  // them at the end of the item.
+  // pipeline they sit in for a whole memory latency); each wave finishes one of the
+  // four and stores it at the item's publishing barrier.
   float p_lse = 0.f, p_delta = 0.f;
   int p_pos = 0, p_q0 = 0;
-  const int* const pos_or_dummy = f.causal ? f.pos : reinterpret_cast<const int*>(f.lse);
-  auto load_scalars = [&](int h, int q0) {
-    const int r = min(q0 + lane, f.Sq - 1);
-    p_lse = f.lse[(int64_t)h * f.lse_ld + r];
-    p_delta = a.delta[(int64_t)h * f.Sq + r];
-    p_pos = pos_or_dummy[f.causal ? f.q_start + r : 0];
-    p_q0 = q0;
+  auto load_scalars = [&](const ItemSrc& src) {
+    p_lse = *src.lse;
+    p_delta = *src.delta;
+    p_pos = *src.pos;
+    p_q0 = src.q0;
   };
   auto store_scalars = [&](int buf) {
     // every wave consumes its loads here, so that none is left in flight on any path
@@ -229,17 +253,15 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
     asm volatile("" :: "v"(p_lse), "v"(p_delta), "v"(p_pos));
     const int r = p_q0 + lane;
     const bool ok = r < f.Sq;
-    const int g = f.q_start + r;
     const float l2 = ok ? p_lse * USP_LOG2E : 0.f;
     const float dl = ok ? -p_delta : 0.f;   // -D: the initial dP accumulator
-    const int dsv = !ok ? 0x7fffffff : (f.causal ? g - p_pos : -0x7fffffff);
-    const int gqv = !ok ? -0x7fffffff : (f.causal ? g : 0x7fffffff);
-    if (wave == 0) {
-      lse2_s[buf][lane] = l2;
-      ndelta_s[buf][lane] = dl;
-      dsq_s[buf][lane] = dsv;
-      gq_s[buf][lane] = gqv;
-    }
+    int klo = 0, khi = f.Sk;                // the row's visible keys [klo, khi)
+    if (f.causal) row_keys_g(f, f.q_start + f.q_stride * r, p_pos, klo, khi);
+    if (!ok) { klo = KBIG; khi = -KBIG; }
+    if (wave == 0) lse2_s[buf][lane] = l2;
+    if (wave == 1) ndelta_s[buf][lane] = dl;
+    if (wave == 2) klo_s[buf][lane] = klo;
+    if (wave == 3) khi_s[buf][lane] = khi;
   };
 
   // items run over all heads' fully visible tiles, then over all heads' other tiles;
@@ -281,14 +303,18 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   };
   bf16x8 ops[PF];   // operand reads in flight, carried from item to item
 
-  // (h, tc): the current item; (hn, tn): the next one (the last item repeats itself)
-  int h = hk * grp, tc = n_full > 0 ? f0 : first_masked;
-  int hn = h, tn = tc;
-  if (n_items > 1) next_item(hn, tn);
+  // item 0 is staged before the loop; nx: where item it+1 comes from (used by item
+  // it), worked out during item it-1; (h2, t2): item it+2 (the last item repeats
+  // itself past the end)
+  int h2 = hk * grp, t2 = n_full > 0 ? f0 : first_masked;
+  const ItemSrc src0 = item_src(h2, t2);
+  if (n_items > 1) next_item(h2, t2);
+  ItemSrc nx = item_src(h2, t2);
+  if (n_items > 2) next_item(h2, t2);
   if (n_items > 0) {
     uint32_t vq = 0;
-    for (int j = 0; j < 16; ++j) dma_step(j, h, tc * BQ, 0, vq);
-    load_scalars(h, tc * BQ);
+    for (int j = 0; j < 16; ++j) dma_step(j, src0, 0, vq);
+    load_scalars(src0);
     wait_vmem();
     store_scalars(0);
     __syncthreads();
@@ -301,7 +327,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   auto run_item = [&](auto mask_tag, int it) {
     constexpr bool MASK = decltype(mask_tag)::v != 0;
     const int buf = it & 1;
-    const int q0n = tn * BQ;
+    ItemSrc nx2;
     // every wave is done with item it-1, which read buffer buf ^ 1: it can be refilled
     // (item it itself was published halfway through item it-1's last slot)
     __syncthreads();
@@ -337,13 +363,13 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
         constexpr int qb = decltype(QB)::v, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
         l4[qb][g4] = *reinterpret_cast<const f32x4*>(&lse2_s[buf][q + 4 * hi]);
         if constexpr (MASK) {
-          const int4 dsv = *reinterpret_cast<const int4*>(&dsq_s[buf][q + 4 * hi]);
-          const int4 gqv = *reinterpret_cast<const int4*>(&gq_s[buf][q + 4 * hi]);
-          const int dsa[4] = {dsv.x, dsv.y, dsv.z, dsv.w};
-          const int gqa[4] = {gqv.x, gqv.y, gqv.z, gqv.w};
+          const int4 lov = *reinterpret_cast<const int4*>(&klo_s[buf][q + 4 * hi]);
+          const int4 hiv = *reinterpret_cast<const int4*>(&khi_s[buf][q + 4 * hi]);
+          const int loa[4] = {lov.x, lov.y, lov.z, lov.w};
+          const int hia[4] = {hiv.x, hiv.y, hiv.z, hiv.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const bool vis = (gk >= dsa[e]) & (gk <= gqa[e]) & key_ok;
+            const bool vis = (kl >= loa[e]) & (kl < hia[e]) & key_ok;
             l4[qb][g4][e] = vis ? l4[qb][g4][e] : INFINITY;
           }
         }
@@ -388,8 +414,9 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
               load_rows(IC<qb>{}, IC<g4>{});
             }
             if constexpr (i >= 8 && i < 12) load_nd(IC<1>{}, IC<i - 8>{}, buf);
-            if constexpr (i % 2 == 1 && i < 32) dma_step(i / 2, hn, q0n, buf ^ 1, vq);   // item it+1
-            if constexpr (i == 2) load_scalars(hn, q0n);                           // its row scalars
+            if constexpr (i % 2 == 1 && i < 32) dma_step(i / 2, nx, buf ^ 1, vq);   // item it+1
+            if constexpr (i == 2) load_scalars(nx);                               // its row scalars
+            if constexpr (i == 50) nx2 = item_src(h2, t2);                      // where item it+2 is
             if constexpr (i == 56) {
               // item it+1 has landed (its DMA was issued in the first half of this item),
               // and so have its row scalars, which go to the other buffer; the barrier
@@ -414,8 +441,8 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
           });
     }
 
-    h = hn; tc = tn;
-    if (it + 2 < n_items) next_item(hn, tn);
+    nx = nx2;
+    if (it + 3 < n_items) next_item(h2, t2);
   };
 #pragma unroll 1
   for (int it = 0; it < n_full; ++it) run_item(IC<0>{}, it);

@@ -54,23 +54,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   const int hk = h / (f.Hq / f.Hkv);
   const int row = qt * BR + wave * 32 + r32;
   const bool row_ok = row < f.Sq;
-  const int gq = f.q_start + row;
 
-  // ---- visible key ranges (global token indices) --------------------------------
-  int ds = 0x7fffffff;
-  int lo = 0x7fffffff, hiex = -0x7fffffff, ds_max = -0x7fffffff, gq_min = 0x7fffffff;
-  if (row_ok) {
-    ds = f.causal ? gq - f.pos[gq] : f.k_start;
-    lo = ds;
-    hiex = f.causal ? gq + 1 : f.k_start + f.Sk;
-    ds_max = ds;
-    gq_min = gq;
-  }
-  const int w_lo = __builtin_amdgcn_readfirstlane(wave_min(lo));
-  const int w_hiex = __builtin_amdgcn_readfirstlane(wave_max(hiex));
-  const int w_dsmax = __builtin_amdgcn_readfirstlane(wave_max(ds_max));
-  const int w_gqmin = __builtin_amdgcn_readfirstlane(wave_min(gq_min));
-  if (lane == 0) { red[wave][0] = w_lo; red[wave][1] = w_hiex; }
+  // ---- visible keys: this lane's row sees local keys [klo, khi); the wave's summary
+  int klo, khi;
+  const WaveKeys wk = wave_keys(f, row, row_ok, klo, khi);
+  if (lane == 0) { red[wave][0] = wk.lo; red[wave][1] = wk.hiex; }
   __syncthreads();
   int g_lo = red[0][0], g_hiex = red[0][1];
 #pragma unroll
@@ -79,8 +67,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   g_hiex = __builtin_amdgcn_readfirstlane(g_hiex);
   // local key range [kb, ke); tiles start on 64-key boundaries (inside one block of
   // the key layout, and on the 16-key groups of the K^T slot order)
-  const int ke = min(g_hiex, f.k_start + f.Sk) - f.k_start;
-  const int kb = (max(g_lo, f.k_start) - f.k_start) & ~(BC - 1);
+  const int ke = g_hiex;
+  const int kb = g_lo & ~(BC - 1);
 
   // ---- Q and dO fragments (B operands of S^T = K Q^T, dP^T = V dO^T):
   // row r32, d = 16 kk + 8 hi + 0..7 ------------------------------------------------
@@ -185,14 +173,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
 
     __builtin_amdgcn_s_setprio(0);
     // ---- mask (boundary tiles only; wave-uniform branch) ---------------------------
-    const int gk0 = f.k_start + kt;
-    const bool full = (kt + BC <= ke) && (!f.causal || (gk0 + BC - 1 <= w_gqmin && gk0 >= w_dsmax));
+    const bool full = kt + BC <= wk.himin && kt >= wk.lomax;   // every row sees every key
     if (!full) {
-      const int klim = ke - kt;
-      // visible: lo_k <= key <= hi_k (no int32 overflow: ds, gq, gk0 are in [0, 2^31));
-      // key = 4 hi + c with c a constant of the register, so the bounds move instead
-      const int lo_k = (f.causal ? max(ds - gk0, kb - kt) : kb - kt) - 4 * hi;
-      const int hi_k = min(f.causal ? gq - gk0 : BC, klim - 1) - 4 * hi;
+      // visible: klo <= kt + key < khi; key = 4 hi + c with c a constant of the
+      // register, so the bounds move instead
+      const int lo_k = klo - kt - 4 * hi;
+      const int hi_k = khi - 1 - kt - 4 * hi;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll

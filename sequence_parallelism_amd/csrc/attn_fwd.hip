@@ -72,26 +72,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   const int hk = h / (a.Hq / a.Hkv);
   const int row = qt * BR + wave * 32 + r32;
   const bool row_ok = row < a.Sq;
-  const int gq = a.q_start + row;
 
   const bf16* __restrict__ qp = reinterpret_cast<const bf16*>(a.q);
 
-  // ---- visible key ranges (global token indices) --------------------------------
-  int ds = 0x7fffffff;
-  int lo = 0x7fffffff, hiex = -0x7fffffff, ds_max = -0x7fffffff, gq_min = 0x7fffffff;
-  if (row_ok) {
-    ds = a.causal ? gq - a.pos[gq] : a.k_start;
-    lo = ds;
-    hiex = a.causal ? gq + 1 : a.k_start + a.Sk;
-    ds_max = ds;
-    gq_min = gq;
-  }
-  // wave-uniform values live in scalar registers
-  const int w_lo = __builtin_amdgcn_readfirstlane(wave_min(lo));
-  const int w_hiex = __builtin_amdgcn_readfirstlane(wave_max(hiex));
-  const int w_dsmax = __builtin_amdgcn_readfirstlane(wave_max(ds_max));
-  const int w_gqmin = __builtin_amdgcn_readfirstlane(wave_min(gq_min));
-  if (lane == 0) { red[wave][0] = w_lo; red[wave][1] = w_hiex; }
+  // ---- visible keys: this lane's row sees local keys [klo, khi); the wave's summary
+  int klo, khi;
+  const WaveKeys wk = wave_keys(a, row, row_ok, klo, khi);
+  if (lane == 0) { red[wave][0] = wk.lo; red[wave][1] = wk.hiex; }
   __syncthreads();
   int g_lo = red[0][0], g_hiex = red[0][1];
 #pragma unroll
@@ -100,8 +87,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   g_hiex = __builtin_amdgcn_readfirstlane(g_hiex);
   // local key range [kb, ke); tiles start on 64-key boundaries (inside one block of
   // the key layout, and on the 16-key groups of the V^T slot order)
-  const int ke = min(g_hiex, a.k_start + a.Sk) - a.k_start;
-  const int kb = (max(g_lo, a.k_start) - a.k_start) & ~(BC - 1);
+  const int ke = g_hiex;
+  const int kb = g_lo & ~(BC - 1);
 
   // ---- Q fragment (B operand of S^T = K Q^T): row r32, d = 16*kk + 8*hi + 0..7
   bf16x8 qf[8];
@@ -186,15 +173,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
           if constexpr (i % 4 == 1) dma_step(i / 4, ktn, buf ^ 1);
         });
     // ---- mask, row max ------------------------------------------------------------
-    const int gk0 = a.k_start + kt;
-    const bool full = (kt + BC <= ke) && (kt >= 0) &&
-                      (!a.causal || (gk0 + BC - 1 <= w_gqmin && gk0 >= w_dsmax));
+    const bool full = kt + BC <= wk.himin && kt >= wk.lomax;   // every row sees every key
     if (!full) {   // wave-uniform branch: per-element mask only on boundary tiles
-      const int klim = ke - kt;
-      // visible: lo_k <= key <= hi_k (no int32 overflow: ds, gq, gk0 are in [0, 2^31));
-      // key = 4 hi + c with c a constant of the register, so the bounds move instead
-      const int lo_k = (a.causal ? max(ds - gk0, kb - kt) : kb - kt) - 4 * hi;
-      const int hi_k = min(a.causal ? gq - gk0 : BC, klim - 1) - 4 * hi;
+      // visible: klo <= kt + key < khi; key = 4 hi + c with c a constant of the
+      // register, so the bounds move instead
+      const int lo_k = klo - kt - 4 * hi;
+      const int hi_k = khi - 1 - kt - 4 * hi;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
@@ -293,13 +277,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
   const float* vp = reinterpret_cast<const float*>(a.v);
   const float q0 = lane < D ? qp[lane] : 0.f;
   const float q1 = lane + 64 < D ? qp[lane + 64] : 0.f;
-  const int gq = a.q_start + row;
-  int kb = 0, ke = a.Sk, ds = 0;
-  if (a.causal) {
-    ds = gq - a.pos[gq];
-    kb = max(ds, a.k_start) - a.k_start;
-    ke = max(kb, min(gq + 1, a.k_start + a.Sk) - a.k_start);
-  }
+  int kb, ke;
+  row_keys(a, row, kb, ke);
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
   for (int j = kb; j < ke; ++j) {
     const float* kr = kp + ((int64_t)j * a.Hkv + hk) * D;

@@ -73,7 +73,10 @@ struct AttnArgs {
   float* lse;
   int64_t lse_ld;
   int32_t Sq, Sk, Hq, Hkv, D;
+  // global token index of local query row r: q_start + q_stride r; of local key j:
+  // k_start + k_stride j (stride 1: a contiguous block; P: a stripe of P ranks)
   int32_t q_start, k_start;
+  int32_t q_stride, k_stride;
   int32_t causal;
   float scale;
   const void* vt;      // bf16 path: V in head-dim-major layout (see transpose.hip)
@@ -82,6 +85,54 @@ struct AttnArgs {
   RowLayout lq;        // bf16 path: rows of q, o (and of dout, dq in the backward)
   RowLayout lk;        // bf16 path: rows of k, v (and of dk, dv)
 };
+// Floor and ceiling of x / s for s > 0 and any sign of x.
+__host__ __device__ __forceinline__ int floor_div(int x, int s) { return x >= 0 ? x / s : -((s - 1 - x) / s); }
+__host__ __device__ __forceinline__ int ceil_div(int x, int s) { return -floor_div(-x, s); }
+
+// Keys visible to local query row `row` (< Sq), as a local key range [lo, hiex)
+// clipped to [0, Sk) (empty when hiex <= lo).  Causal with position_ids: the row's
+// global index gq and its document start gq - pos[gq] bound the visible global key
+// indices, gq - pos[gq] <= k_start + k_stride j <= gq; otherwise every key.  With
+// k_stride 1 the bounds are plain differences; a stripe divides by its stride.
+__device__ __forceinline__ void row_keys(const AttnArgs& a, int row, int& lo, int& hiex) {
+  if (!a.causal) {
+    lo = 0;
+    hiex = a.Sk;
+    return;
+  }
+  const int gq = a.q_start + a.q_stride * row;
+  const int ds = gq - a.pos[gq];
+  if (a.k_stride == 1) {
+    lo = ds - a.k_start;
+    hiex = gq - a.k_start + 1;
+  } else {
+    lo = ceil_div(ds - a.k_start, a.k_stride);
+    hiex = floor_div(gq - a.k_start, a.k_stride) + 1;
+  }
+  lo = max(lo, 0);
+  hiex = min(hiex, a.Sk);
+}
+
+// The same from the row's global index and its position_ids value (pos of gq).
+__device__ __forceinline__ void row_keys_g(const AttnArgs& a, int gq, int posv, int& lo, int& hiex) {
+  const int ds = gq - posv;
+  if (a.k_stride == 1) {
+    lo = ds - a.k_start;
+    hiex = gq - a.k_start + 1;
+  } else {
+    lo = ceil_div(ds - a.k_start, a.k_stride);
+    hiex = floor_div(gq - a.k_start, a.k_stride) + 1;
+  }
+  lo = max(lo, 0);
+  hiex = min(hiex, a.Sk);
+}
+
+// First local query row that sees local key j or a later one (causal): the smallest
+// row with q_start + q_stride row >= k_start + k_stride j, clipped at 0.
+__device__ __forceinline__ int first_row_seeing(const AttnArgs& a, int j) {
+  return max(ceil_div(a.k_start + a.k_stride * j - a.q_start, a.q_stride), 0);
+}
+
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t s);
 size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hkv, int32_t D, int bf16_path);
 // fills a.vt, a.vt_ld and a.q_order from the workspace base (bf16 path)

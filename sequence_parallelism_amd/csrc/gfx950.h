@@ -100,4 +100,25 @@ __device__ __forceinline__ int wave_max(int x) {
   return x;
 }
 
+// Sentinel bound for key ranges: far outside any index, with room for the small
+// offsets the masks add to it.
+constexpr int KBIG = 0x3fffffff;
+
+// Visible local keys of this lane's query row (row_keys; empty [0, 0) past Sq), and
+// the wave's summary: [lo, hiex) covers every key some row of the wave sees, [lomax,
+// himin) only keys that every row sees (empty rows make it empty).
+struct WaveKeys { int lo, hiex, lomax, himin; };
+__device__ __forceinline__ WaveKeys wave_keys(const AttnArgs& a, int row, bool row_ok, int& klo, int& khi) {
+  klo = 0;
+  khi = 0;
+  if (row_ok) row_keys(a, row, klo, khi);
+  const bool any = row_ok && klo < khi;
+  WaveKeys w;
+  w.lo = __builtin_amdgcn_readfirstlane(wave_min(any ? klo : KBIG));
+  w.hiex = __builtin_amdgcn_readfirstlane(wave_max(any ? khi : -KBIG));
+  w.lomax = __builtin_amdgcn_readfirstlane(wave_max(row_ok ? klo : -KBIG));
+  w.himin = __builtin_amdgcn_readfirstlane(wave_min(row_ok ? khi : KBIG));
+  return w;
+}
+
 }  // namespace gfx950

@@ -23,27 +23,27 @@ constexpr int MAXU = 12288;     // units sorted in LDS; larger launches keep nat
 __device__ int kv_block_work(const AttnArgs& f, int b, int bkv, int bq, int n_qtiles) {
   if (!f.causal) return n_qtiles;
   const int k0 = b * bkv;
-  const int gk_first = f.k_start + k0;
-  const int gk_last = f.k_start + min(k0 + bkv, f.Sk) - 1;
-  const int t0 = min(max(gk_first - f.q_start, 0) / bq, n_qtiles);
-  int lo = t0, hi = n_qtiles;   // first tile whose first row starts its document after gk_last
+  const int k_last = min(k0 + bkv, f.Sk) - 1;
+  const int t0 = min(first_row_seeing(f, k0) / bq, n_qtiles);
+  int lo = t0, hi = n_qtiles;   // first tile whose first row's visible keys start after k_last
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    const int g = f.q_start + mid * bq;
-    if (g - f.pos[g] > gk_last) hi = mid; else lo = mid + 1;
+    int lo_k, hiex_k;
+    row_keys(f, mid * bq, lo_k, hiex_k);
+    if (lo_k > k_last) hi = mid; else lo = mid + 1;
   }
   return lo - t0;
 }
 
 // Work of query tile t of BR rows for the forward and dQ kernels: the number of keys
-// its rows can see, from the first row's document start to the last row.
+// its rows can see, from the first row's first visible key to the last row's last.
 __device__ int q_tile_work(const AttnArgs& f, int t, int br) {
   if (!f.causal) return f.Sk;
   const int r0 = t * br, r1 = min(r0 + br, f.Sq) - 1;
-  const int g0 = f.q_start + r0, g1 = f.q_start + r1;
-  const int lo = max(g0 - f.pos[g0], f.k_start);
-  const int hiex = min(g1 + 1, f.k_start + f.Sk);
-  return max(hiex - lo, 0);
+  int lo0, hiex0, lo1, hiex1;
+  row_keys(f, r0, lo0, hiex0);
+  row_keys(f, r1, lo1, hiex1);
+  return max(hiex1 - lo0, 0);
 }
 
 // KIND 0: key blocks (p0 = keys per block, p1 = rows per query tile, p2 = query tiles);

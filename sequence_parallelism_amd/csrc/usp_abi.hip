@@ -61,6 +61,7 @@ AttnArgs make_args(const void* q, const void* k, const void* v, int64_t Sq, int6
   a.q = q; a.k = k; a.v = v; a.pos = pos; a.o = o; a.lse = lse; a.lse_ld = lse_ld;
   a.Sq = (int32_t)Sq; a.Sk = (int32_t)Sk; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
   a.q_start = (int32_t)q_start; a.k_start = (int32_t)k_start;
+  a.q_stride = 1; a.k_stride = 1;
   a.causal = causal ? 1 : 0;
   a.scale = scale;
   a.vt = nullptr;
