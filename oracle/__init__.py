@@ -20,6 +20,9 @@ in float64 numpy with no blocking, fusion or reordering beyond the definition:
                    softmax (Ring Attention page, same section).
 * ``ring``      -- the four-device ring simulation of the Ring Attention page,
                    in the page's raw-exp form and in the running-max form.
+* ``striped``   -- the striped token layout of the same page's Striped Attention
+                   remark (rank r holds tokens r, r + P, ...), attention between
+                   two stripes, and the ring over stripes.
 
 Pins (tests/test_oracle_*.py) tie each function to facts the pages and the
 mathematics fix; see the test modules for which pin covers which function.
@@ -30,10 +33,12 @@ from .attention import (visible_mask, attention_fwd, attention_bwd,
                         attention_probs, causal_visible_pairs)
 from .merge import lse_merge
 from .ring import ring_sim_raw, ring_sim_online, full_attention_noncausal
+from .striped import seq_to_stripe, stripe_to_seq, striped_pair_fwd, striped_ring_fwd
 
 __all__ = [
     "seq_to_head", "head_to_seq", "seq_to_head_elementwise",
     "visible_mask", "attention_fwd", "attention_bwd", "attention_probs",
     "causal_visible_pairs", "lse_merge",
     "ring_sim_raw", "ring_sim_online", "full_attention_noncausal",
+    "seq_to_stripe", "stripe_to_seq", "striped_pair_fwd", "striped_ring_fwd",
 ]

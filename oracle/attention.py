@@ -15,8 +15,10 @@ A row that sees no key gets O_i = 0 and LSE_i = -inf.
 
 Visibility (aitoolresearcher Ulysses SP review, section 3: the causal mask is carried
 by O(n) position_ids instead of an n x n mask).  Reading adopted: query row i is the
-global token gq = q_start + i, key j is gk = k_start + j; position_ids restart at 0
-at each packed document, so gq - pos[gq] is the first token of gq's document and
+global token gq = q_start + q_stride i, key j is gk = k_start + k_stride j (strides 1
+for contiguous blocks; P for the striped layout of the Ring Attention glossary page,
+where rank r holds tokens r, r + P, ...); position_ids restart at 0 at each packed
+document, so gq - pos[gq] is the first token of gq's document and
 
     visible(i, j)  <=>  gq - pos[gq] <= gk <= gq      (causal)
     visible(i, j)  <=>  True                          (non-causal)
@@ -68,13 +70,14 @@ def visible_mask(gq, gk, pos, causal):
     return (gk[None, :] >= start[:, None]) & (gk[None, :] <= gq[:, None])
 
 
-def _key_range(rows_g, pos, causal, k_start, Sk):
-    """Local key interval [lo, hi) that can be visible to any of the global rows."""
+def _key_range(rows_g, pos, causal, k_start, Sk, k_stride=1):
+    """Local key interval [lo, hi) that can be visible to any of the global rows:
+    local keys j with min(start) <= k_start + k_stride j <= max(gq)."""
     if not causal:
         return 0, Sk
     start = rows_g - np.asarray(pos, dtype=np.int64)[rows_g]
-    lo = max(int(start.min()), k_start) - k_start
-    hi = min(int(rows_g.max()) + 1, k_start + Sk) - k_start
+    lo = max(-((k_start - int(start.min())) // k_stride), 0)       # ceil division
+    hi = min((int(rows_g.max()) - k_start) // k_stride + 1, Sk)    # floor division
     return lo, max(lo, hi)
 
 
@@ -125,7 +128,7 @@ def _check(q, k, v, pos, causal):
 
 
 def attention_fwd(q, k, v, pos=None, q_start=0, k_start=0, causal=False,
-                  scale=None, rows=None, threads=None):
+                  scale=None, rows=None, threads=None, q_stride=1, k_stride=1):
     """Exact attention.  q [Sq][Hq][D], k, v [Sk][Hkv][D] (any float dtype).
 
     ``rows``: optional local query rows to evaluate (default all).
@@ -148,10 +151,10 @@ def attention_fwd(q, k, v, pos=None, q_start=0, k_start=0, causal=False,
         hk = h // grp
         for sel in _chunks(idx, Sk):
             def job(h=h, hk=hk, sel=sel):
-                rg = q_start + rows[sel]
-                lo, hi = _key_range(rg, pos, causal, k_start, Sk)
+                rg = q_start + q_stride * rows[sel]
+                lo, hi = _key_range(rg, pos, causal, k_start, Sk, k_stride)
                 P, m, l = _row_probs(q[rows[sel], h], k[lo:hi, hk], rg,
-                                     k_start + np.arange(lo, hi), pos, causal, scale)
+                                     k_start + k_stride * np.arange(lo, hi), pos, causal, scale)
                 O[sel, h] = P @ v[lo:hi, hk]
                 LSE[h, sel] = np.where(np.isfinite(m), m + np.log(np.where(l > 0, l, 1.0)),
                                        _NEG_INF)
@@ -160,7 +163,8 @@ def attention_fwd(q, k, v, pos=None, q_start=0, k_start=0, causal=False,
     return O, LSE
 
 
-def attention_probs(q, k, pos=None, q_start=0, k_start=0, causal=False, scale=None):
+def attention_probs(q, k, pos=None, q_start=0, k_start=0, causal=False, scale=None,
+                    q_stride=1, k_stride=1):
     """Normalised probabilities P [Hq][Sq][Sk] (small inputs only)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -169,14 +173,14 @@ def attention_probs(q, k, pos=None, q_start=0, k_start=0, causal=False, scale=No
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     out = np.zeros((Hq, Sq, Sk))
     for h in range(Hq):
-        P, _, _ = _row_probs(q[:, h], k[:, h // (Hq // Hkv)], q_start + np.arange(Sq),
-                             k_start + np.arange(Sk), pos, causal, scale)
+        P, _, _ = _row_probs(q[:, h], k[:, h // (Hq // Hkv)], q_start + q_stride * np.arange(Sq),
+                             k_start + k_stride * np.arange(Sk), pos, causal, scale)
         out[h] = P
     return out
 
 
 def attention_bwd(q, k, v, do, pos=None, q_start=0, k_start=0, causal=False,
-                  scale=None, rows=None, threads=None):
+                  scale=None, rows=None, threads=None, q_stride=1, k_stride=1):
     """Analytic gradients of the forward above for upstream gradient dO [Sq][Hq][D].
 
     ``rows``: optional local query rows whose contributions are taken (default
@@ -202,10 +206,10 @@ def attention_bwd(q, k, v, do, pos=None, q_start=0, k_start=0, causal=False,
         for sel in _chunks(idx, Sk):
             def job(h=h, hk=hk, sel=sel):
                 r = rows[sel]
-                rg = q_start + r
-                lo, hi = _key_range(rg, pos, causal, k_start, Sk)
+                rg = q_start + q_stride * r
+                lo, hi = _key_range(rg, pos, causal, k_start, Sk, k_stride)
                 kh, vh = k[lo:hi, hk], v[lo:hi, hk]
-                P, _, _ = _row_probs(q[r, h], kh, rg, k_start + np.arange(lo, hi),
+                P, _, _ = _row_probs(q[r, h], kh, rg, k_start + k_stride * np.arange(lo, hi),
                                      pos, causal, scale)
                 dO = do[r, h]
                 O = P @ vh
