@@ -6,7 +6,9 @@
  *     done here as a local permutation on one GPU;
  *   - exact blockwise softmax attention (forward and backward) over that share,
  *     with the causal / packed-document mask given by O(n) position_ids;
- *   - the merge of partial (O, LSE) results by the cumulative softmax.
+ *   - the merge of partial (O, LSE) results by the cumulative softmax;
+ *   - the striped token layout (rank r of P holds tokens r, r + P, ...), its
+ *     permutes and attention between two stripes.
  *
  * Conventions for every entry point
  *   - Pointers named q, k, v, o, dout, dq, dk, dv, workspace, lse, position_ids,
@@ -35,7 +37,7 @@
 extern "C" {
 #endif
 
-#define USP_ABI_VERSION 2
+#define USP_ABI_VERSION 3
 
 typedef enum {
   USP_OK = 0,
@@ -225,6 +227,54 @@ usp_status usp_ulysses_attn_bwd(const void* xq, const void* xk, const void* xv, 
                                 int32_t group, const int32_t* position_ids, int32_t causal,
                                 float softmax_scale, usp_dtype in_dtype, void* dxq, void* dxk,
                                 void* dxv, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Striped layout.
+ *
+ * Ultralytics glossary "Ring Attention", section "Como funciona la atencion en
+ * anillo" (its Striped Attention remark): with a causal mask, contiguous blocks leave
+ * the ranks that hold early queries idle; giving every rank tokens spread evenly over
+ * the sequence balances the work.  Here rank r of P holds tokens r, r + P, r + 2P,
+ * ... (S / P of them, in order).
+ *
+ * usp_seq_to_stripe_permute: dst [P][S/P][H][D] with dst[r][j] = src[r + P j];
+ * usp_stripe_to_seq_permute: the exact inverse, dst [S][H][D].
+ *   src, dst: dtype elements, not overlapping; S a multiple of P (NOT_DIVISIBLE),
+ *   S H D < 2^31 (UNSUPPORTED), pointers aligned to the element size (MISALIGNED).
+ *   Bit-exact copies.
+ * ------------------------------------------------------------------------- */
+usp_status usp_seq_to_stripe_permute(void* dst, const void* src, int32_t P, int64_t S, int32_t H, int32_t D,
+                                     usp_dtype dtype, void* stream);
+usp_status usp_stripe_to_seq_permute(void* dst, const void* src, int32_t P, int64_t S, int32_t H, int32_t D,
+                                     usp_dtype dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Attention between the queries of stripe q_rank and the keys / values of stripe
+ * k_rank (one step of a ring over striped ranks), forward and backward.
+ *
+ * Same section as above.  Exactly blockattn_fwd / blockattn_bwd with Sq = Sk =
+ * S_stripe, except that local query row r is global token q_rank + P r and local key
+ * j is global token k_rank + P j: key j is visible to row r iff
+ * g - pos[g] <= k_rank + P j <= g with g = q_rank + P r (causal), every key
+ * otherwise.  position_ids: int32 over the whole sequence (P S_stripe tokens, global
+ * order).  Other arguments, layouts, outputs (O, LSE of this stripe pair; dQ, dK,
+ * dV of this pair, to be summed over pairs by the caller), workspace sizes
+ * (blockattn_*_workspace_size with Sq = Sk = S_stripe) and errors as for blockattn_fwd
+ * / blockattn_bwd; in addition P < 1 or a rank outside [0, P) is BAD_SHAPE, and
+ * P S_stripe >= 2^31 is UNSUPPORTED.  Merging the P partial results of a query
+ * stripe with lse_merge gives the exact attention of its tokens.
+ * ------------------------------------------------------------------------- */
+usp_status usp_striped_attn_fwd(const void* q, const void* k, const void* v, int64_t S_stripe, int32_t Hq,
+                                int32_t Hkv, int32_t D, int32_t P, int32_t q_rank, int32_t k_rank,
+                                const int32_t* position_ids, int32_t causal, float softmax_scale,
+                                usp_dtype in_dtype, void* o, usp_dtype o_dtype, float* lse, int64_t lse_ld,
+                                void* workspace, size_t workspace_bytes, void* stream);
+usp_status usp_striped_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                int64_t lse_ld, const void* dout, int64_t S_stripe, int32_t Hq, int32_t Hkv,
+                                int32_t D, int32_t P, int32_t q_rank, int32_t k_rank,
+                                const int32_t* position_ids, int32_t causal, float softmax_scale,
+                                usp_dtype in_dtype, void* dq, void* dk, void* dv, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -44,6 +44,18 @@ SIGNATURES = {
                                      ctypes.c_size_t, _vp]),
     "lse_merge": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _c_int64, _vp, ctypes.c_int, _vp,
                                  _c_int64, _c_int64, _c_int32, _c_int32, _vp]),
+    "usp_seq_to_stripe_permute": (ctypes.c_int, [_vp, _vp, _c_int32, _c_int64, _c_int32, _c_int32,
+                                                 ctypes.c_int, _vp]),
+    "usp_stripe_to_seq_permute": (ctypes.c_int, [_vp, _vp, _c_int32, _c_int64, _c_int32, _c_int32,
+                                                 ctypes.c_int, _vp]),
+    "usp_striped_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, _c_int64, _c_int32, _c_int32, _c_int32,
+                                            _c_int32, _c_int32, _c_int32, _vp, _c_int32, _c_float,
+                                            ctypes.c_int, _vp, ctypes.c_int, _vp, _c_int64, _vp,
+                                            ctypes.c_size_t, _vp]),
+    "usp_striped_attn_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_int64, _vp, _c_int64, _c_int32,
+                                            _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _vp,
+                                            _c_int32, _c_float, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                            ctypes.c_size_t, _vp]),
     "usp_ulysses_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, _c_int32, _c_int64, _c_int32, _c_int32,
                                             _c_int32, _c_int32, _vp, _c_int32, _c_float, ctypes.c_int,
                                             _vp, _vp, _c_int64, _vp, ctypes.c_size_t, _vp]),
@@ -282,6 +294,88 @@ def ulysses_attn_bwd(xq, xk, xv, o_seq, lse, xdo, group, position_ids=None, caus
     return dxq, dxk, dxv
 
 
+# ---- striped layout: rank r holds tokens r, r + P, r + 2P, ... ----------------------
+
+def seq_to_stripe(x, P, out=None, stream=None):
+    """[S][H][D] -> [P][S/P][H][D] with out[r][j] = x[r + P j]."""
+    import torch
+    lib = load()
+    _need(x, "x")
+    S, H, D = x.shape
+    out = torch.empty((P, S // P, H, D), dtype=x.dtype, device=x.device) if out is None else out
+    _need(out, "out")
+    _check("usp_seq_to_stripe_permute",
+           lib.usp_seq_to_stripe_permute(_ptr(out), _ptr(x), P, S, H, D, _dtype_code(x), _stream(stream)))
+    return out
+
+
+def stripe_to_seq(y, out=None, stream=None):
+    """[P][S/P][H][D] -> [S][H][D], the inverse of seq_to_stripe."""
+    import torch
+    lib = load()
+    _need(y, "y")
+    P, n, H, D = y.shape
+    out = torch.empty((P * n, H, D), dtype=y.dtype, device=y.device) if out is None else out
+    _need(out, "out")
+    _check("usp_stripe_to_seq_permute",
+           lib.usp_stripe_to_seq_permute(_ptr(out), _ptr(y), P, P * n, H, D, _dtype_code(y), _stream(stream)))
+    return out
+
+
+def striped_attn_fwd(q, k, v, P, q_rank, k_rank, position_ids=None, causal=True, scale=None, o=None,
+                     lse=None, o_dtype=None, workspace=None, stream=None):
+    """Stripe q_rank's queries q [n][Hq][D] against stripe k_rank's keys and values
+    k, v [n][Hkv][D] -> (o [n][Hq][D], lse [Hq][n] float32)."""
+    import torch
+    lib = load()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm)
+    n, Hq, D = q.shape
+    Hkv = k.shape[1]
+    scale = D ** -0.5 if scale is None else float(scale)
+    if o is None:
+        o = torch.empty((n, Hq, D), dtype=o_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((Hq, n), dtype=torch.float32, device=q.device)
+    _need(o, "o")
+    need = fwd_workspace_bytes(n, n, Hq, Hkv, D, _dtype_code(q))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("usp_striped_attn_fwd",
+           lib.usp_striped_attn_fwd(_ptr(q), _ptr(k), _ptr(v), n, Hq, Hkv, D, P, q_rank, k_rank,
+                                    _ptr(position_ids), int(bool(causal)), scale, _dtype_code(q),
+                                    _ptr(o), _dtype_code(o), _ptr(lse), lse.stride(0), _ptr(workspace),
+                                    ws_bytes, _stream(stream)))
+    return o, lse
+
+
+def striped_attn_bwd(q, k, v, o, lse, dout, P, q_rank, k_rank, position_ids=None, causal=True,
+                     scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of striped_attn_fwd for this stripe pair, with o and lse
+    the query stripe's final (merged) output and log-sum-exp."""
+    import torch
+    lib = load()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, nm)
+    n, Hq, D = q.shape
+    Hkv = k.shape[1]
+    scale = D ** -0.5 if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = bwd_workspace_bytes(n, n, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check("usp_striped_attn_bwd",
+           lib.usp_striped_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), lse.stride(0),
+                                    _ptr(dout), n, Hq, Hkv, D, P, q_rank, k_rank, _ptr(position_ids),
+                                    int(bool(causal)), scale, _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)))
+    return dq, dk, dv
+
+
 def lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
     """In place: (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_part, lse_part))."""
     lib = load()
@@ -296,5 +390,6 @@ def lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
 
 
 __all__ = ["load", "seq_to_head", "head_to_seq", "blockattn_fwd", "blockattn_bwd",
-           "ulysses_attn_fwd", "ulysses_attn_bwd",
+           "ulysses_attn_fwd", "ulysses_attn_bwd", "seq_to_stripe", "stripe_to_seq",
+           "striped_attn_fwd", "striped_attn_bwd",
            "fwd_workspace_bytes", "bwd_workspace_bytes", "lse_merge", "UspError", "BF16", "F32", "SIGNATURES"]

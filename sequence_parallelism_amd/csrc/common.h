@@ -31,6 +31,18 @@ struct PermuteArgs {
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 
+// Contiguous [S][H][D] <-> striped [P][S/P][H][D] (rank r: tokens r, r + P, ...).
+struct StripeArgs {
+  void* dst;
+  const void* src;
+  int32_t P;
+  int64_t S;          // tokens in total, a multiple of P
+  int32_t H, D;
+  int32_t esize;
+  int32_t to_stripe;  // 1: contiguous -> striped, 0: striped -> contiguous
+};
+hipError_t launch_stripe(const StripeArgs& a, hipStream_t s);
+
 // Where token `row`, head `h` of a token-major tensor starts (elements; head dim 128
 // on the MFMA paths): block b = row / blk_rows, then
 //   b * blk_stride + (row - b * blk_rows) * row_stride + (head0 + h) * 128.

@@ -107,7 +107,67 @@ hipError_t launch_typed(const PermuteArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Striped layout (Ultralytics glossary "Ring Attention", the Striped Attention
+// paragraph of "Como funciona la atencion en anillo"): rank r of P holds tokens
+// r, r + P, r + 2P, ... of the sequence.  Striped row r*n + j (n = S/P tokens per
+// rank) is contiguous row r + P*j; every row is one run of `row_vec` vectors.  One
+// thread per vector, UNROLL vectors per thread; a row index needs two fast divisions.
+template <typename V, int UNROLL>
+__global__ __launch_bounds__(256) void stripe_kernel(char* __restrict__ dst, const char* __restrict__ src,
+                                                     uint64_t n_vec, FastDiv row_vec, FastDiv per_rank,
+                                                     int32_t P, int32_t to_stripe) {
+  const uint64_t i0 = (uint64_t)blockIdx.x * (256u * UNROLL) + threadIdx.x;
+  V buf[UNROLL];
+  int64_t so[UNROLL], co[UNROLL];
+  bool ok[UNROLL];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const uint64_t idx = i0 + (uint64_t)u * 256u;
+    ok[u] = idx < n_vec;
+    const uint32_t ix = ok[u] ? (uint32_t)idx : 0u;
+    const uint32_t srow = row_vec.div(ix);               // striped row r*n + j
+    const uint32_t w = ix - srow * row_vec.d;
+    const uint32_t r = per_rank.div(srow);
+    const uint32_t jj = srow - r * per_rank.d;
+    const uint32_t crow = r + (uint32_t)P * jj;          // contiguous row
+    so[u] = ((int64_t)srow * row_vec.d + w) * (int64_t)sizeof(V);
+    co[u] = ((int64_t)crow * row_vec.d + w) * (int64_t)sizeof(V);
+  }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u)
+    if (ok[u]) buf[u] = *reinterpret_cast<const V*>(src + (to_stripe ? co[u] : so[u]));
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u)
+    if (ok[u]) __builtin_nontemporal_store(buf[u], reinterpret_cast<V*>(dst + (to_stripe ? so[u] : co[u])));
+}
+
+template <typename V>
+hipError_t launch_stripe_typed(const StripeArgs& a, hipStream_t stream) {
+  constexpr int UNROLL = 4;
+  const int64_t row_bytes = (int64_t)a.H * a.D * a.esize;
+  const uint32_t rv = (uint32_t)(row_bytes / (int64_t)sizeof(V));
+  const uint64_t n_vec = (uint64_t)a.S * rv;
+  FastDiv fr, fn;
+  fr.init(rv);
+  fn.init((uint32_t)(a.S / a.P));
+  const uint64_t blocks = (n_vec + 256u * UNROLL - 1) / (256u * UNROLL);
+  hipLaunchKernelGGL((stripe_kernel<V, UNROLL>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<char*>(a.dst), reinterpret_cast<const char*>(a.src), n_vec, fr, fn,
+                     a.P, a.to_stripe);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_stripe(const StripeArgs& a, hipStream_t stream) {
+  const int64_t row_bytes = (int64_t)a.H * a.D * a.esize;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(a.dst) | reinterpret_cast<uintptr_t>(a.src);
+  if (a.S == 0) return hipSuccess;
+  if (row_bytes % 16 == 0 && al % 16 == 0) return launch_stripe_typed<u32x4>(a, stream);
+  if (row_bytes % 8 == 0 && al % 8 == 0) return launch_stripe_typed<u32x2>(a, stream);
+  if (row_bytes % 4 == 0 && al % 4 == 0) return launch_stripe_typed<uint32_t>(a, stream);
+  return launch_stripe_typed<uint16_t>(a, stream);
+}
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   const int64_t run_bytes = (int64_t)(a.H / a.P) * a.D * a.esize;

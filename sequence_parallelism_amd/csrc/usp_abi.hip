@@ -31,7 +31,7 @@ usp_status check_permute(const void* dst, const void* src, int32_t P, int64_t S_
 usp_status check_attn(const void* q, const void* k, const void* v, int64_t Sq, int64_t Sk,
                       int32_t Hq, int32_t Hkv, int32_t D, const int32_t* pos, int64_t q_start,
                       int64_t k_start, int32_t causal, usp_dtype in_dt, const void* o,
-                      const float* lse, int64_t lse_ld) {
+                      const float* lse, int64_t lse_ld, int64_t q_stride = 1, int64_t k_stride = 1) {
   // a pointer to an empty tensor may be NULL
   if (Sq > 0 && (!q || !o || !lse)) return USP_ERR_NULL_POINTER;
   if (Sk > 0 && (!k || !v)) return USP_ERR_NULL_POINTER;
@@ -42,7 +42,7 @@ usp_status check_attn(const void* q, const void* k, const void* v, int64_t Sq, i
   if (lse_ld < Sq) return USP_ERR_BAD_SHAPE;
   if (Hq % Hkv) return USP_ERR_NOT_DIVISIBLE;
   // global token indices and element offsets are 32/64-bit in the kernels
-  if (q_start + Sq > I32_MAX || k_start + Sk > I32_MAX) return USP_ERR_UNSUPPORTED;
+  if (q_start + q_stride * Sq > I32_MAX || k_start + k_stride * Sk > I32_MAX) return USP_ERR_UNSUPPORTED;
   if (Sq * Hq > I32_MAX || Sk * Hkv > I32_MAX) return USP_ERR_UNSUPPORTED;
   if (in_dt == USP_BF16 && D != 128) return USP_ERR_UNSUPPORTED;
   if (in_dt == USP_F32 && D > 128) return USP_ERR_UNSUPPORTED;
@@ -71,6 +71,69 @@ AttnArgs make_args(const void* q, const void* k, const void* v, int64_t Sq, int6
   a.lk = contiguous_rows(Hkv);
   return a;
 }
+
+}  // namespace
+
+namespace {
+
+// Forward / backward over a query block and a key block whose local row r (key j) is
+// global token q_start + q_stride r (k_start + k_stride j).
+usp_status attn_fwd_impl(const void* q, const void* k, const void* v, int64_t Sq, int64_t Sk, int32_t Hq,
+                         int32_t Hkv, int32_t D, const int32_t* position_ids, int64_t q_start,
+                         int64_t q_stride, int64_t k_start, int64_t k_stride, int32_t causal,
+                         float softmax_scale, usp_dtype in_dtype, void* o, usp_dtype o_dtype, float* lse,
+                         int64_t lse_ld, void* workspace, size_t workspace_bytes, void* stream) {
+  usp_status st = check_attn(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal,
+                             in_dtype, o, lse, lse_ld, q_stride, k_stride);
+  if (st != USP_OK) return st;
+  if (bad_dtype(o_dtype) || (in_dtype == USP_F32 && o_dtype != USP_F32)) return USP_ERR_BAD_DTYPE;
+  if (o_dtype == USP_F32 && !aligned(o, 16) && in_dtype == USP_BF16) return USP_ERR_MISALIGNED;
+  const size_t need = attn_fwd_workspace_bytes(Sq, Sk, Hkv, D, in_dtype == USP_BF16);
+  if (need > 0 && !workspace) return USP_ERR_NULL_POINTER;
+  if (workspace && !aligned(workspace, 16)) return USP_ERR_MISALIGNED;
+  if (workspace_bytes < need) return USP_ERR_WORKSPACE_TOO_SMALL;
+  AttnArgs a = make_args(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal,
+                         softmax_scale, o, lse, lse_ld);
+  a.q_stride = (int32_t)q_stride;
+  a.k_stride = (int32_t)k_stride;
+  if (in_dtype == USP_BF16) attn_fwd_workspace_layout(a, workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (in_dtype == USP_BF16) return hip_status(launch_attn_fwd_bf16(a, o_dtype == USP_F32, s));
+  return hip_status(launch_attn_fwd_f32(a, s));
+}
+
+usp_status attn_bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         int64_t lse_ld, const void* dout, int64_t Sq, int64_t Sk, int32_t Hq,
+                         int32_t Hkv, int32_t D, const int32_t* position_ids, int64_t q_start,
+                         int64_t q_stride, int64_t k_start, int64_t k_stride, int32_t causal,
+                         float softmax_scale, usp_dtype in_dtype, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  usp_status st = check_attn(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal,
+                             in_dtype, o, lse, lse_ld, q_stride, k_stride);
+  if (st != USP_OK) return st;
+  if (Sq > 0 && (!dout || !dq)) return USP_ERR_NULL_POINTER;
+  if (Sk > 0 && (!dk || !dv)) return USP_ERR_NULL_POINTER;
+  if (!workspace && attn_bwd_workspace_bytes(Sq, Sk, Hq, Hkv, D) > 0) return USP_ERR_NULL_POINTER;
+  if (in_dtype != USP_BF16) return USP_ERR_UNSUPPORTED;
+  if (!attn_bwd_supported(Sq, Sk, Hq, Hkv)) return USP_ERR_UNSUPPORTED;
+  if (!(aligned(dout, 16) && aligned(dq, 16) && aligned(dk, 8) && aligned(dv, 8) &&
+        aligned(workspace, 256)))
+    return USP_ERR_MISALIGNED;
+  const size_t need = attn_bwd_workspace_bytes(Sq, Sk, Hq, Hkv, D);
+  if (workspace_bytes < need) return USP_ERR_WORKSPACE_TOO_SMALL;
+  AttnBwdArgs a;
+  a.f = make_args(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal, softmax_scale,
+                  const_cast<void*>(o), const_cast<float*>(lse), lse_ld);
+  a.f.q_stride = (int32_t)q_stride;
+  a.f.k_stride = (int32_t)k_stride;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  attn_bwd_workspace_layout(a, workspace);
+  return hip_status(launch_attn_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 
 }  // namespace
 
@@ -123,21 +186,8 @@ usp_status blockattn_fwd(const void* q, const void* k, const void* v, int64_t Sq
                          int64_t q_start, int64_t k_start, int32_t causal, float softmax_scale,
                          usp_dtype in_dtype, void* o, usp_dtype o_dtype, float* lse, int64_t lse_ld,
                          void* workspace, size_t workspace_bytes, void* stream) {
-  usp_status st = check_attn(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal,
-                             in_dtype, o, lse, lse_ld);
-  if (st != USP_OK) return st;
-  if (bad_dtype(o_dtype) || (in_dtype == USP_F32 && o_dtype != USP_F32)) return USP_ERR_BAD_DTYPE;
-  if (o_dtype == USP_F32 && !aligned(o, 16) && in_dtype == USP_BF16) return USP_ERR_MISALIGNED;
-  const size_t need = attn_fwd_workspace_bytes(Sq, Sk, Hkv, D, in_dtype == USP_BF16);
-  if (need > 0 && !workspace) return USP_ERR_NULL_POINTER;
-  if (workspace && !aligned(workspace, 16)) return USP_ERR_MISALIGNED;
-  if (workspace_bytes < need) return USP_ERR_WORKSPACE_TOO_SMALL;
-  AttnArgs a = make_args(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal,
-                         softmax_scale, o, lse, lse_ld);
-  if (in_dtype == USP_BF16) attn_fwd_workspace_layout(a, workspace);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (in_dtype == USP_BF16) return hip_status(launch_attn_fwd_bf16(a, o_dtype == USP_F32, s));
-  return hip_status(launch_attn_fwd_f32(a, s));
+  return attn_fwd_impl(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, 1, k_start, 1, causal,
+                       softmax_scale, in_dtype, o, o_dtype, lse, lse_ld, workspace, workspace_bytes, stream);
 }
 
 usp_status blockattn_bwd_workspace_size(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D,
@@ -154,28 +204,9 @@ usp_status blockattn_bwd(const void* q, const void* k, const void* v, const void
                          int64_t k_start, int32_t causal, float softmax_scale, usp_dtype in_dtype,
                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                          void* stream) {
-  usp_status st = check_attn(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal,
-                             in_dtype, o, lse, lse_ld);
-  if (st != USP_OK) return st;
-  if (Sq > 0 && (!dout || !dq)) return USP_ERR_NULL_POINTER;
-  if (Sk > 0 && (!dk || !dv)) return USP_ERR_NULL_POINTER;
-  if (!workspace && attn_bwd_workspace_bytes(Sq, Sk, Hq, Hkv, D) > 0) return USP_ERR_NULL_POINTER;
-  if (in_dtype != USP_BF16) return USP_ERR_UNSUPPORTED;
-  if (!attn_bwd_supported(Sq, Sk, Hq, Hkv)) return USP_ERR_UNSUPPORTED;
-  if (!(aligned(dout, 16) && aligned(dq, 16) && aligned(dk, 8) && aligned(dv, 8) &&
-        aligned(workspace, 256)))
-    return USP_ERR_MISALIGNED;
-  const size_t need = attn_bwd_workspace_bytes(Sq, Sk, Hq, Hkv, D);
-  if (workspace_bytes < need) return USP_ERR_WORKSPACE_TOO_SMALL;
-  AttnBwdArgs a;
-  a.f = make_args(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal, softmax_scale,
-                  const_cast<void*>(o), const_cast<float*>(lse), lse_ld);
-  a.dout = dout;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  attn_bwd_workspace_layout(a, workspace);
-  return hip_status(launch_attn_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream)));
+  return attn_bwd_impl(q, k, v, o, lse, lse_ld, dout, Sq, Sk, Hq, Hkv, D, position_ids, q_start, 1,
+                       k_start, 1, causal, softmax_scale, in_dtype, dq, dk, dv, workspace,
+                       workspace_bytes, stream);
 }
 
 usp_status lse_merge(void* o_acc, usp_dtype acc_dtype, float* lse_acc, int64_t lse_acc_ld,
@@ -279,6 +310,58 @@ usp_status usp_ulysses_attn_bwd(const void* xq, const void* xk, const void* xv, 
   a.dv = dxv;
   attn_bwd_workspace_layout(a, workspace);
   return hip_status(launch_attn_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---- Striped layout: rank r holds tokens r, r + P, r + 2P, ... ---------------------
+
+extern "C" {
+
+usp_status usp_seq_to_stripe_permute(void* dst, const void* src, int32_t P, int64_t S, int32_t H, int32_t D,
+                                     usp_dtype dtype, void* stream) {
+  if (bad_dtype(dtype)) return USP_ERR_BAD_DTYPE;
+  if (P < 1 || S < 0 || H < 1 || D < 1) return USP_ERR_BAD_SHAPE;
+  if (S % P) return USP_ERR_NOT_DIVISIBLE;
+  if ((!dst || !src) && S > 0) return USP_ERR_NULL_POINTER;
+  if (S * H * (int64_t)D > I32_MAX) return USP_ERR_UNSUPPORTED;
+  if (!aligned(dst, esize(dtype)) || !aligned(src, esize(dtype))) return USP_ERR_MISALIGNED;
+  StripeArgs a{dst, src, P, S, H, D, esize(dtype), 1};
+  return hip_status(launch_stripe(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+usp_status usp_stripe_to_seq_permute(void* dst, const void* src, int32_t P, int64_t S, int32_t H, int32_t D,
+                                     usp_dtype dtype, void* stream) {
+  if (bad_dtype(dtype)) return USP_ERR_BAD_DTYPE;
+  if (P < 1 || S < 0 || H < 1 || D < 1) return USP_ERR_BAD_SHAPE;
+  if (S % P) return USP_ERR_NOT_DIVISIBLE;
+  if ((!dst || !src) && S > 0) return USP_ERR_NULL_POINTER;
+  if (S * H * (int64_t)D > I32_MAX) return USP_ERR_UNSUPPORTED;
+  if (!aligned(dst, esize(dtype)) || !aligned(src, esize(dtype))) return USP_ERR_MISALIGNED;
+  StripeArgs a{dst, src, P, S, H, D, esize(dtype), 0};
+  return hip_status(launch_stripe(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+usp_status usp_striped_attn_fwd(const void* q, const void* k, const void* v, int64_t S_stripe, int32_t Hq,
+                                int32_t Hkv, int32_t D, int32_t P, int32_t q_rank, int32_t k_rank,
+                                const int32_t* position_ids, int32_t causal, float softmax_scale,
+                                usp_dtype in_dtype, void* o, usp_dtype o_dtype, float* lse, int64_t lse_ld,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (P < 1 || q_rank < 0 || q_rank >= P || k_rank < 0 || k_rank >= P) return USP_ERR_BAD_SHAPE;
+  return attn_fwd_impl(q, k, v, S_stripe, S_stripe, Hq, Hkv, D, position_ids, q_rank, P, k_rank, P, causal,
+                       softmax_scale, in_dtype, o, o_dtype, lse, lse_ld, workspace, workspace_bytes, stream);
+}
+
+usp_status usp_striped_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                int64_t lse_ld, const void* dout, int64_t S_stripe, int32_t Hq, int32_t Hkv,
+                                int32_t D, int32_t P, int32_t q_rank, int32_t k_rank,
+                                const int32_t* position_ids, int32_t causal, float softmax_scale,
+                                usp_dtype in_dtype, void* dq, void* dk, void* dv, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (P < 1 || q_rank < 0 || q_rank >= P || k_rank < 0 || k_rank >= P) return USP_ERR_BAD_SHAPE;
+  return attn_bwd_impl(q, k, v, o, lse, lse_ld, dout, S_stripe, S_stripe, Hq, Hkv, D, position_ids, q_rank, P,
+                       k_rank, P, causal, softmax_scale, in_dtype, dq, dk, dv, workspace, workspace_bytes,
+                       stream);
 }
 
 }  // extern "C"

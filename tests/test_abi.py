@@ -32,7 +32,9 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("usp_seq_to_head_permute", "usp_head_to_seq_permute", "blockattn_fwd",
-              "blockattn_bwd", "lse_merge", "usp_ulysses_attn_fwd", "usp_ulysses_attn_bwd"):
+              "blockattn_bwd", "lse_merge", "usp_ulysses_attn_fwd", "usp_ulysses_attn_bwd",
+              "usp_seq_to_stripe_permute", "usp_stripe_to_seq_permute", "usp_striped_attn_fwd",
+              "usp_striped_attn_bwd"):
         assert n in names
 
 
@@ -48,7 +50,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.usp_abi_version() == 2
+    assert lib.usp_abi_version() == 3
     for code in range(9):
         s = lib.usp_status_string(code).decode()
         assert s and s != "unknown status"
@@ -161,3 +163,36 @@ def test_ulysses_fused_validation(lib):
     assert bwd(ws=A + 16) == MISAL
     assert bwd(wsb=16) == WS
     assert bwd(S_l=128) == UNSUP
+
+
+def test_striped_validation(lib):
+    """Stripe permutes and stripe-pair attention: layout and rank checks on top of the
+    blockattn checks."""
+    for fn in ("usp_seq_to_stripe_permute", "usp_stripe_to_seq_permute"):
+        f = getattr(lib, fn)
+        assert f(None, A, 4, 64, 2, 128, 0, None) == NULLP
+        assert f(A, A, 4, 66, 2, 128, 0, None) == NOTDIV       # S not a multiple of P
+        assert f(A, A, 0, 64, 2, 128, 0, None) == SHAPE
+        assert f(A, A, 4, 64, 2, 128, 5, None) == DTYPE
+        assert f(A + 1, A, 4, 64, 2, 128, 0, None) == MISAL
+        assert f(A, A, 4, 1 << 24, 16, 128, 0, None) == UNSUP  # S H D >= 2^31
+        assert f(None, None, 4, 0, 2, 128, 0, None) == OK      # empty: nothing to do
+
+    n = ctypes.c_size_t(1 << 30)
+
+    def fwd(P=4, qr=1, kr=2, S=256, pos=A, ws=A):
+        return lib.usp_striped_attn_fwd(A, A, A, S, 4, 1, 128, P, qr, kr, pos, 1, 0.1, 0, A, 0, A, S,
+                                        ws, n.value, None)
+    assert fwd(P=0) == SHAPE
+    assert fwd(qr=4) == SHAPE
+    assert fwd(kr=-1) == SHAPE
+    assert fwd(pos=None) == NULLP
+    assert fwd(ws=None) == NULLP
+    assert fwd(S=(1 << 29)) == UNSUP                            # P S_stripe >= 2^31
+
+    def bwd(P=4, qr=0, kr=3, dq=A):
+        return lib.usp_striped_attn_bwd(A, A, A, A, A, 256, A, 256, 4, 1, 128, P, qr, kr, A, 1, 0.1, 0,
+                                        dq, A, A, A, n.value, None)
+    assert bwd(qr=-1) == SHAPE
+    assert bwd(kr=4) == SHAPE
+    assert bwd(dq=None) == NULLP
