@@ -335,6 +335,7 @@ def extra_measurements(torch, usp, dev, g):
     res["lse_merge_us"] = round(ms * 1e3, 2)
     del acc, acc_l, parts, pl
     res.update(ring_measurement(torch, usp, dev, g))
+    res.update(striped_measurement(torch, usp, dev, g))
     res.update(allgather_measurement(torch, usp, dev, g))
     return res
 
@@ -398,6 +399,85 @@ def ring_measurement(torch, usp, dev, g):
     return {"ring256k_fwd_ms": round(ms_f, 2), "ring256k_fwd_TFLOPs": round(flop_f / ms_f / 1e9, 1),
             "ring256k_bwd_ms": round(ms_b, 2),
             "ring256k_bwd_TFLOPs": round(2.5 * flop_f / ms_b / 1e9, 1)}
+
+
+def striped_measurement(torch, usp, dev, g):
+    """The 256K single-document ring over 16 ranks, contiguous blocks against stripes
+    (rank r holding tokens r, r + 16, ...), emulated on one GPU.  Every (query rank,
+    key rank) call of the forward and of the backward is timed on its own; a ring step
+    lasts as long as its slowest rank, so the ring's time is the sum over steps of
+    the per-step maximum (a contiguous pair above the diagonal has no visible key and
+    is skipped).  The work is the same in both layouts; the stripes balance it."""
+    S, H, P = 262144, 2, 16
+    n = S // P
+    mk = lambda: torch.randn((S, H, D), generator=g, device=dev).to(torch.bfloat16)
+    q, k, v, do = mk(), mk(), mk(), mk()
+    pos = torch.arange(S, dtype=torch.int32, device=dev)
+    po = torch.empty((n, H, D), dtype=torch.float32, device=dev)
+    pl = torch.empty((H, n), dtype=torch.float32, device=dev)
+    wsf = torch.empty(usp.fwd_workspace_bytes(n, n, H, H, D), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(usp.bwd_workspace_bytes(n, n, H, H, D), dtype=torch.uint8, device=dev)
+    pq = torch.empty((n, H, D), dtype=torch.bfloat16, device=dev)
+    pk, pv = torch.empty_like(pq), torch.empty_like(pq)
+    acc = torch.zeros((P, n, H, D), dtype=torch.float32, device=dev)
+    acc_l = torch.full((P, H, n), -float("inf"), dtype=torch.float32, device=dev)
+
+    def per_call(calls):
+        """calls: {(i, j): fn}; returns {(i, j): ms}, after one untimed pass."""
+        for fn in calls.values():
+            fn()
+        torch.cuda.synchronize()
+        evs = {key: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for key in calls}
+        for key, fn in calls.items():
+            evs[key][0].record()
+            fn()
+            evs[key][1].record()
+        torch.cuda.synchronize()
+        return {key: e[0].elapsed_time(e[1]) for key, e in evs.items()}
+
+    def ring_time(ms):
+        return sum(max(ms.get((i, (i - t) % P), 0.0) for i in range(P)) for t in range(P))
+
+    res = {}
+    # contiguous blocks: pairs j <= i
+    blk = lambda t, i: t[i * n:(i + 1) * n]
+    for i in range(P):
+        for j in range(i + 1):
+            usp.blockattn_fwd(blk(q, i), blk(k, j), blk(v, j), pos, q_start=i * n, k_start=j * n,
+                              o=po, lse=pl, workspace=wsf)
+            usp.lse_merge(acc[i], acc_l[i], po, pl)
+    o_c = acc.to(torch.bfloat16)
+    fwd_c = {(i, j): (lambda i=i, j=j: usp.blockattn_fwd(
+        blk(q, i), blk(k, j), blk(v, j), pos, q_start=i * n, k_start=j * n, o=po, lse=pl, workspace=wsf))
+        for i in range(P) for j in range(i + 1)}
+    bwd_c = {(i, j): (lambda i=i, j=j: usp.blockattn_bwd(
+        blk(q, i), blk(k, j), blk(v, j), o_c[i], acc_l[i], blk(do, i), pos, q_start=i * n,
+        k_start=j * n, dq=pq, dk=pk, dv=pv, workspace=wsb))
+        for i in range(P) for j in range(i + 1)}
+    # stripes: every pair
+    qs, ks, vs, dos = (usp.seq_to_stripe(t, P) for t in (q, k, v, do))
+    acc.zero_()
+    acc_l.fill_(-float("inf"))
+    for i in range(P):
+        for j in range(P):
+            usp.striped_attn_fwd(qs[i], ks[j], vs[j], P, i, j, pos, o=po, lse=pl, workspace=wsf)
+            usp.lse_merge(acc[i], acc_l[i], po, pl)
+    o_s = acc.to(torch.bfloat16)
+    fwd_s = {(i, j): (lambda i=i, j=j: usp.striped_attn_fwd(
+        qs[i], ks[j], vs[j], P, i, j, pos, o=po, lse=pl, workspace=wsf)) for i in range(P) for j in range(P)}
+    bwd_s = {(i, j): (lambda i=i, j=j: usp.striped_attn_bwd(
+        qs[i], ks[j], vs[j], o_s[i], acc_l[i], dos[i], P, i, j, pos, dq=pq, dk=pk, dv=pv, workspace=wsb))
+        for i in range(P) for j in range(P)}
+    t = {name: per_call(c) for name, c in (("fc", fwd_c), ("bc", bwd_c), ("fs", fwd_s), ("bs", bwd_s))}
+    ring_c = ring_time(t["fc"]) + ring_time(t["bc"])
+    ring_s = ring_time(t["fs"]) + ring_time(t["bs"])
+    res["ring16_256k_contiguous_fwd_bwd_ms"] = round(ring_c, 2)
+    res["ring16_256k_striped_fwd_bwd_ms"] = round(ring_s, 2)
+    res["ring16_256k_striped_speedup"] = round(ring_c / ring_s, 3)
+    res["ring16_256k_serial_contiguous_ms"] = round(sum(t["fc"].values()) + sum(t["bc"].values()), 2)
+    res["ring16_256k_serial_striped_ms"] = round(sum(t["fs"].values()) + sum(t["bs"].values()), 2)
+    return res
 
 
 def allgather_measurement(torch, usp, dev, g):

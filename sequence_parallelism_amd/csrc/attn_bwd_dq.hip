@@ -26,15 +26,18 @@ namespace {
 using namespace gfx950;
 
 constexpr int HD = 128;          // head dim
-constexpr int NW = 8;            // wavefronts per workgroup
-constexpr int BR = 32 * NW;      // query rows per workgroup
 constexpr int BC = 64;           // keys per LDS tile
 constexpr int PF = 4;            // LDS operand reads in flight ahead of their MFMA
 constexpr int TILE = BC * HD;    // elements of one staged tile (16 KB)
 constexpr int NXCD = 8;          // MI355X dispatches workgroup i to XCD i % 8
-static_assert(TILE / 8 == 2 * NW * 64, "a staged tile is two 64-lane DMA loads per wave");
 
+// NW wavefronts (32 query rows each) per workgroup: 8 normally, 4 when a call has
+// too few 256-row tiles to give every CU a workgroup.
+template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int n_qtiles) {
+  constexpr int BR = 32 * NW;              // query rows per workgroup
+  constexpr int NL = TILE / 8 / (NW * 64); // 64-lane DMA loads per wave per staged tile
+  static_assert(NL * NW * 64 * 8 == TILE, "a staged tile is a whole number of loads per wave");
   // per buffer: K [64 keys][128], V [64 keys][128] (swz16), K^T [128][64 positions] (swz8)
   __shared__ __attribute__((aligned(16))) bf16 stage[2][3 * TILE];
   __shared__ int red[NW][2];
@@ -99,29 +102,29 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   asm volatile("" :: "v"(lse2), "v"(dlt));
   const float sl2 = f.scale * USP_LOG2E;
 
-  // ---- staging by LDS-DMA: tile u (K, V, K^T), load i (0..1) of wave w covers
-  // physical chunks [(8i + w) * 64, +64), lane l the chunk (8i + w) * 64 + l:
-  //   K, V: key row 32i + 4w + l/16, physical chunk l%16;
-  //   K^T:  head-dim row 64i + 8w + l/8, physical chunk l%8.
-  // The swizzle depends on the row modulo 16 only, so one lane offset serves both loads.
+  // ---- staging by LDS-DMA: tile u (K, V, K^T), load i (0..NL-1) of wave w covers
+  // physical chunks [(NW i + w) * 64, +64), lane l the chunk (NW i + w) * 64 + l:
+  //   K, V: key row 4 NW i + 4w + l/16, physical chunk l%16;
+  //   K^T:  head-dim row 8 NW i + 8w + l/8, physical chunk l%8.
+  // The swizzles depend on the row modulo 16 only, so one lane offset serves all loads.
   const uint32_t kr0 = (uint32_t)(4 * wave + (lane >> 4));
   const uint32_t k_lc = (uint32_t)((((lane & 15) ^ swz16(kr0)) << 3) * 2);
   const uint32_t rowkB = (uint32_t)f.lk.row_stride * 2;          // bytes per k / v row
   const int td0 = 8 * wave + (lane >> 3);
   const uint32_t t_off = (uint32_t)((td0 * a.sk_pad + (((lane & 7) ^ swz8(td0)) << 3)) * 2);
   const uint32_t stage_lds = lds_addr(&stage[0][0]);
-  auto dma_step = [&](int s, int kt, int buf) {   // s = 2u + i
-    const int u = s >> 1, i = s & 1;
+  auto dma_step = [&](int s, int kt, int buf) {   // s = NL u + i
+    const int u = s / NL, i = s % NL;
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         stage_lds + (uint32_t)(((buf * 3 + u) * TILE + (NW * i + wave) * 512) * 2));
     if (u < 2) {   // keys past Sk are clamped to the last key (the mask zeroes them)
       const uint32_t lim = (uint32_t)(f.Sk - 1 - kt);
-      const uint32_t voff = min(kr0 + 32 * i, lim) * rowkB + k_lc;
+      const uint32_t voff = min(kr0 + 4 * NW * i, lim) * rowkB + k_lc;
       const char* base = reinterpret_cast<const char*>(u == 0 ? f.k : f.v) + rows_off(f.lk, kt, hk) * 2;
       dma16(base, voff, lds);
     } else {
       const char* base = reinterpret_cast<const char*>(a.kt) +
-                         (((int64_t)hk * HD + 64 * i) * a.sk_pad + kt) * 2;
+                         (((int64_t)hk * HD + 8 * NW * i) * a.sk_pad + kt) * 2;
       dma16(base, t_off, lds);
     }
   };
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   for (int i = 0; i < 4; ++i) dqacc[i] = f32x16{};
 
   if (kb < ke) {
-    for (int s = 0; s < 6; ++s) dma_step(s, kb, 0);
+    for (int s = 0; s < 3 * NL; ++s) dma_step(s, kb, 0);
     wait_vmem();
     __syncthreads();
   }
@@ -168,7 +171,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
         },
         [&](auto I) {
           constexpr int i = decltype(I)::v;
-          if constexpr (i % 4 == 1 && i / 4 < 6) dma_step(i / 4, ktn, buf ^ 1);
+          // the 3 NL loads spread over the 32 MFMAs
+          constexpr int every = 32 / (4 * NL);
+          if constexpr (i % every == 1 % every && i / every < 3 * NL) dma_step(i / every, ktn, buf ^ 1);
         });
 
     __builtin_amdgcn_s_setprio(0);
@@ -236,15 +241,27 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
 
 // a must carry the workspace regions of attn_bwd_workspace_layout, with D and the
 // head-dim-major k already written (launch_attn_bwd_bf16 does both first).
-int attn_bwd_dq_rows_per_tile() { return BR; }
+// the smallest tile height the launcher uses (sizes the tile-order workspace)
+int attn_bwd_dq_rows_per_tile() { return 128; }
 
-hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, hipStream_t stream) {
+namespace {
+template <int NW>
+hipError_t launch_dq_nw(const AttnBwdArgs& a, hipStream_t stream) {
+  constexpr int BR = 32 * NW;
   const AttnArgs& f = a.f;
-  if (f.Sq == 0) return hipSuccess;
   const int n_qtiles = (f.Sq + BR - 1) / BR;
   hipError_t e = launch_schedule_q_tiles(f, n_qtiles, BR, a.dq_order, stream);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)(((n_qtiles + NXCD - 1) / NXCD) * NXCD * f.Hq));
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, grid, dim3(NW * 64), 0, stream, a, n_qtiles);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<NW>), grid, dim3(NW * 64), 0, stream, a, n_qtiles);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, hipStream_t stream) {
+  const AttnArgs& f = a.f;
+  if (f.Sq == 0) return hipSuccess;
+  const int64_t wg256 = (int64_t)((f.Sq + 255) / 256) * f.Hq;
+  if (wg256 < device_cu_count()) return launch_dq_nw<4>(a, stream);
+  return launch_dq_nw<8>(a, stream);
 }

@@ -41,17 +41,20 @@ namespace {
 using namespace gfx950;
 
 constexpr int HD = 128;          // head dim of the MFMA path
-constexpr int NW = 8;            // wavefronts per workgroup
-constexpr int BR = 32 * NW;      // query rows per workgroup
 constexpr int BC = 64;           // keys per LDS tile
 constexpr int PF = 4;            // LDS operand reads in flight ahead of their MFMA
 constexpr float RESCALE_TH = 8.f;  // log2 of the largest P allowed before the max moves
 constexpr int TILE = BC * HD;    // elements of one staged tile (16 KB)
-static_assert(TILE / 8 == 2 * NW * 64, "a staged tile is two 64-lane DMA loads per wave");
 constexpr int NXCD = 8;          // MI355X dispatches workgroup i to XCD i % 8
 
-template <bool O_F32>
+// NW wavefronts (32 query rows each) per workgroup: 8 normally (one workgroup per
+// CU, 2 waves per SIMD); 4 when a call has too few query tiles to fill the chip
+// with 256-row workgroups (two 128-row workgroups then share a CU).
+template <bool O_F32, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int n_qtiles) {
+  constexpr int BR = 32 * NW;              // query rows per workgroup
+  constexpr int NL = TILE / 8 / (NW * 64); // 64-lane DMA loads per wave per staged tile
+  static_assert(NL * NW * 64 * 8 == TILE, "a staged tile is a whole number of loads per wave");
   // per buffer: K [64 keys][128] (swz16), V^T [128][64 positions] (swz8)
   __shared__ __attribute__((aligned(16))) bf16 stage[2][2 * TILE];
   __shared__ int red[NW][2];
@@ -105,27 +108,27 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
     for (int kk = 0; kk < 8; ++kk) asm volatile("" :: "v"(qf[kk]));
   }
 
-  // ---- staging by LDS-DMA: tile u (K, V^T), load i (0..1) of wave w covers physical
-  // chunks [(8i + w) * 64, +64), lane l the chunk (8i + w) * 64 + l:
-  //   K:   key row 32i + 4w + l/16, physical chunk l%16;
-  //   V^T: head-dim row 64i + 8w + l/8, physical chunk l%8.
-  // The swizzle depends on the row modulo 16 only, so one lane offset serves both loads.
+  // ---- staging by LDS-DMA: tile u (K, V^T), load i (0..NL-1) of wave w covers
+  // physical chunks [(NW i + w) * 64, +64), lane l the chunk (NW i + w) * 64 + l:
+  //   K:   key row 4 NW i + 4w + l/16, physical chunk l%16;
+  //   V^T: head-dim row 8 NW i + 8w + l/8, physical chunk l%8.
+  // The swizzles depend on the row modulo 16 only, so one lane offset serves all loads.
   const uint32_t kr0 = (uint32_t)(4 * wave + (lane >> 4));
   const uint32_t k_lc = (uint32_t)((((lane & 15) ^ swz16(kr0)) << 3) * 2);
   const uint32_t rowkB = (uint32_t)a.lk.row_stride * 2;          // bytes per k row
   const int td0 = 8 * wave + (lane >> 3);
   const uint32_t t_off = (uint32_t)((td0 * a.vt_ld + (((lane & 7) ^ swz8(td0)) << 3)) * 2);
   const uint32_t stage_lds = lds_addr(&stage[0][0]);
-  auto dma_step = [&](int s, int kt, int buf) {   // s = 2u + i
-    const int u = s >> 1, i = s & 1;
+  auto dma_step = [&](int s, int kt, int buf) {   // s = NL u + i
+    const int u = s / NL, i = s % NL;
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         stage_lds + (uint32_t)(((buf * 2 + u) * TILE + (NW * i + wave) * 512) * 2));
     if (u == 0) {   // keys past Sk are clamped to the last key (the mask zeroes them)
       const uint32_t lim = (uint32_t)(a.Sk - 1 - kt);
-      const uint32_t voff = min(kr0 + 32 * i, lim) * rowkB + k_lc;
+      const uint32_t voff = min(kr0 + 4 * NW * i, lim) * rowkB + k_lc;
       dma16(reinterpret_cast<const char*>(a.k) + rows_off(a.lk, kt, hk) * 2, voff, lds);
     } else {        // the padded copy covers every position of the tile
-      dma16(reinterpret_cast<const char*>(a.vt) + (((int64_t)hk * HD + 64 * i) * a.vt_ld + kt) * 2,
+      dma16(reinterpret_cast<const char*>(a.vt) + (((int64_t)hk * HD + 8 * NW * i) * a.vt_ld + kt) * 2,
             t_off, lds);
     }
   };
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   const int vbase = r32 * BC + ((hi ^ swz8(r32)) << 3);
 
   if (kb < ke) {
-    for (int s = 0; s < 4; ++s) dma_step(s, kb, 0);
+    for (int s = 0; s < 2 * NL; ++s) dma_step(s, kb, 0);
     wait_vmem();
     __syncthreads();
   }
@@ -170,7 +173,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
         },
         [&](auto I) {
           constexpr int i = decltype(I)::v;
-          if constexpr (i % 4 == 1) dma_step(i / 4, ktn, buf ^ 1);
+          constexpr int every = 16 / (2 * NL);   // the 2 NL loads spread over 16 MFMAs
+          if constexpr (i % every == 1 % every) dma_step(i / every, ktn, buf ^ 1);
         });
     // ---- mask, row max ------------------------------------------------------------
     const bool full = kt + BC <= wk.himin && kt >= wk.lomax;   // every row sees every key
@@ -308,10 +312,11 @@ namespace {
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 }  // namespace
 
-// workspace: V^T copy [Hkv][D][padded Sk] bf16, then the query-tile order
+// workspace: V^T copy [Hkv][D][padded Sk] bf16, then the query-tile order (sized for
+// the 128-row tiles of the 4-wave variant)
 size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hkv, int32_t D, int bf16_path) {
   if (!bf16_path) return 0;
-  const size_t n_qtiles = (size_t)((Sq + BR - 1) / BR);
+  const size_t n_qtiles = (size_t)((Sq + 127) / 128);
   return align256((size_t)Hkv * D * transpose_perm16_padded_len(Sk) * sizeof(bf16)) +
          n_qtiles * sizeof(int);
 }
@@ -323,6 +328,32 @@ void attn_fwd_workspace_layout(AttnArgs& a, void* base) {
   a.q_order = reinterpret_cast<int*>(p + align256((size_t)a.Hkv * a.D * a.vt_ld * sizeof(bf16)));
 }
 
+namespace {
+template <int NW>
+hipError_t launch_fwd_nw(const AttnArgs& a, int o_f32, hipStream_t stream) {
+  constexpr int BR = 32 * NW;
+  const int n_qtiles = (a.Sq + BR - 1) / BR;
+  hipError_t e = launch_schedule_q_tiles(a, n_qtiles, BR, a.q_order, stream);
+  if (e != hipSuccess) return e;
+  dim3 grid((unsigned)(((n_qtiles + NXCD - 1) / NXCD) * NXCD * a.Hq));
+  if (o_f32)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<true, NW>), grid, dim3(NW * 64), 0, stream, a, n_qtiles);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, NW>), grid, dim3(NW * 64), 0, stream, a, n_qtiles);
+  return hipGetLastError();
+}
+}  // namespace
+
+// Compute units of the current device (the 4-wave variant is chosen when 256-row
+// workgroups would not give every CU one).
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
 // a.vt must point at a workspace of attn_fwd_workspace_bytes; it is filled here.
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t stream) {
   if (a.Sq == 0) return hipSuccess;
@@ -330,15 +361,9 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t stream
     hipError_t e = launch_transpose_perm16(a.v, a.lk, a.Sk, a.Hkv, const_cast<void*>(a.vt), stream);
     if (e != hipSuccess) return e;
   }
-  const int n_qtiles = (a.Sq + BR - 1) / BR;
-  hipError_t e = launch_schedule_q_tiles(a, n_qtiles, BR, a.q_order, stream);
-  if (e != hipSuccess) return e;
-  dim3 grid((unsigned)(((n_qtiles + NXCD - 1) / NXCD) * NXCD * a.Hq));
-  if (o_f32)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, grid, dim3(NW * 64), 0, stream, a, n_qtiles);
-  else
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, grid, dim3(NW * 64), 0, stream, a, n_qtiles);
-  return hipGetLastError();
+  const int64_t wg256 = (int64_t)((a.Sq + 255) / 256) * a.Hq;
+  if (wg256 < device_cu_count()) return launch_fwd_nw<4>(a, o_f32, stream);
+  return launch_fwd_nw<8>(a, o_f32, stream);
 }
 
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream) {

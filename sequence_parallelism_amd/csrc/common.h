@@ -146,6 +146,7 @@ __device__ __forceinline__ int first_row_seeing(const AttnArgs& a, int j) {
 }
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t s);
+int device_cu_count();
 size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hkv, int32_t D, int bf16_path);
 // fills a.vt, a.vt_ld and a.q_order from the workspace base (bf16 path)
 void attn_fwd_workspace_layout(AttnArgs& a, void* base);
