@@ -34,6 +34,8 @@
 // f32 kernel (small head dims, e.g. the four-device ring example): one wavefront
 // per (query row, head), keys visited one at a time with the same running
 // (m, l, O) recurrence in fp32 VALU arithmetic.
+#include <algorithm>
+
 #include "gfx950.h"
 
 namespace {
@@ -50,7 +52,9 @@ constexpr int NXCD = 8;          // MI355X dispatches workgroup i to XCD i % 8
 // NW wavefronts (32 query rows each) per workgroup: 8 normally (one workgroup per
 // CU, 2 waves per SIMD); 4 when a call has too few query tiles to fill the chip
 // with 256-row workgroups (two 128-row workgroups then share a CU).
-template <bool O_F32, int NW>
+// SPLIT: the workgroup takes chunk c of its tile's key range (a.ksplit chunks) and
+// writes a normalised partial O and LSE for the combine pass.
+template <bool O_F32, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int n_qtiles) {
   constexpr int BR = 32 * NW;              // query rows per workgroup
   constexpr int NL = TILE / 8 / (NW * 64); // 64-lane DMA loads per wave per staged tile
@@ -67,9 +71,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   // every NXCD-th in decreasing order of work (schedule.hip), so concurrent
   // workgroups on an XCD read the same key/value tiles from its L2, every XCD gets a
   // fair share, and the heaviest tiles start first.
+  // With split key ranges the chunks of a tile follow its heads.
   const int xcd = blockIdx.x % NXCD, j = blockIdx.x / NXCD;
   const int h = j % a.Hq;
-  const int rank = (j / a.Hq) * NXCD + xcd;
+  const int nch = SPLIT ? a.ksplit : 1;
+  const int chunk = SPLIT ? (j / a.Hq) % nch : 0;
+  const int rank = (j / a.Hq / nch) * NXCD + xcd;
   if (rank >= n_qtiles) return;                             // grid padding (whole workgroup)
   const int qt = min(max(a.q_order[rank], 0), n_qtiles - 1);   // a permutation of the tiles
   const int hk = h / (a.Hq / a.Hkv);
@@ -90,8 +97,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   g_hiex = __builtin_amdgcn_readfirstlane(g_hiex);
   // local key range [kb, ke); tiles start on 64-key boundaries (inside one block of
   // the key layout, and on the 16-key groups of the V^T slot order)
-  const int ke = g_hiex;
-  const int kb = g_lo & ~(BC - 1);
+  int ke = g_hiex;
+  int kb = g_lo & ~(BC - 1);
+  if (SPLIT) {   // chunk `chunk` of [kb, ke): equal lengths, multiples of the tile
+    const int len = ((ke > kb ? ceil_div(ke - kb, nch) : 0) + BC - 1) & ~(BC - 1);
+    kb += chunk * len;
+    ke = min(ke, kb + len);
+  }
 
   // ---- Q fragment (B operand of S^T = K Q^T): row r32, d = 16*kk + 8*hi + 0..7
   bf16x8 qf[8];
@@ -244,8 +256,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 ---------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse_out = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * USP_LN2 : -INFINITY;
   if (row_ok) {
-    const int64_t obase = rows_off(a.lq, row, h);
+    const int64_t slot = ((int64_t)h * n_qtiles + qt) * nch + chunk;   // partial of this chunk
+    const int rr = wave * 32 + r32;
+    const int64_t obase = SPLIT ? (slot * BR + rr) * HD : rows_off(a.lq, row, h);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -253,7 +268,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
         const int d = 32 * db + 8 * g4 + 4 * hi;
         const f32x4 val = {oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv,
                            oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
-        if (O_F32) {
+        if (SPLIT) {
+          *reinterpret_cast<f32x4*>(a.o_part + obase + d) = val;
+        } else if (O_F32) {
           *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + obase + d) = val;
         } else {
           const bf16x4 ov = {(bf16)val[0], (bf16)val[1], (bf16)val[2], (bf16)val[3]};
@@ -261,10 +278,54 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
         }
       }
     }
-    if (hi == 0)
-      a.lse[(int64_t)h * a.lse_ld + row] =
-          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * USP_LN2 : -INFINITY;
+    if (hi == 0) {
+      if (SPLIT) a.lse_part[slot * BR + rr] = lse_out;
+      else a.lse[(int64_t)h * a.lse_ld + row] = lse_out;
+    }
   }
+}
+
+// ---- combine of split key ranges: per (head, row), the cumulative-softmax merge of
+// its tile's chunk partials (as lse_merge, over ksplit parts) -------------------------
+template <bool O_F32, int BR>
+__global__ __launch_bounds__(256) void attn_fwd_combine_kernel(AttnArgs a, int n_qtiles) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rid = gid >> 4;                 // (head, row), 16 lanes of 8 elements each
+  const int sub = threadIdx.x & 15;
+  if (rid >= (int64_t)a.Hq * a.Sq) return;
+  const int h = (int)(rid / a.Sq), row = (int)(rid - (int64_t)h * a.Sq);
+  const int qt = row / BR, rr = row - qt * BR;
+  const int nch = a.ksplit;
+  const int64_t slot0 = ((int64_t)h * n_qtiles + qt) * nch;
+  float m = -INFINITY;
+  for (int c = 0; c < nch; ++c) m = fmaxf(m, a.lse_part[(slot0 + c) * BR + rr]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (m != -INFINITY) {
+    for (int c = 0; c < nch; ++c) {
+      const float w = __expf(a.lse_part[(slot0 + c) * BR + rr] - m);   // 0 for an empty chunk
+      if (w == 0.f) continue;
+      const float* src = a.o_part + ((slot0 + c) * BR + rr) * HD + 8 * sub;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { acc[e] += w * x0[e]; acc[4 + e] += w * x1[e]; }
+      den += w;
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const int64_t obase = rows_off(a.lq, row, h) + 8 * sub;
+  if (O_F32) {
+    float* o = reinterpret_cast<float*>(a.o) + obase;
+    *reinterpret_cast<f32x4*>(o) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+  } else {
+    bf16x8 ov;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ov[e] = (bf16)(acc[e] * inv);
+    *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.o) + obase) = ov;
+  }
+  if (sub == 0) a.lse[(int64_t)h * a.lse_ld + row] = den > 0.f ? m + __logf(den) : -INFINITY;
 }
 
 // ---- fp32 path: one wavefront per (query row, head) ----------------------------
@@ -312,35 +373,73 @@ namespace {
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 }  // namespace
 
-// workspace: V^T copy [Hkv][D][padded Sk] bf16, then the query-tile order (sized for
-// the 128-row tiles of the 4-wave variant)
-size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hkv, int32_t D, int bf16_path) {
+// Key-range split of a call: 1 (none) unless its 256-row workgroups (times heads)
+// would leave CUs idle and its keys are many; then chunks for about four workgroups
+// per CU, at most 16.
+int fwd_ksplit(int64_t Sq, int64_t Sk, int32_t Hq) {
+  const int64_t wg = (int64_t)((Sq + 255) / 256) * Hq;
+  const int cus = device_cu_count();
+  if (wg == 0 || wg >= cus || Sk < 2048) return 1;
+  return (int)std::min<int64_t>(16, (4 * (int64_t)cus + wg - 1) / wg);
+}
+
+// workspace: V^T copy [Hkv][D][padded Sk] bf16, the query-tile order (sized for the
+// 128-row tiles of the 4-wave variant), and with a key-range split the partials
+// o_part [Hq][tiles][ksplit][256][128] and lse_part [Hq][tiles][ksplit][256] (fp32)
+size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D, int bf16_path) {
   if (!bf16_path) return 0;
   const size_t n_qtiles = (size_t)((Sq + 127) / 128);
-  return align256((size_t)Hkv * D * transpose_perm16_padded_len(Sk) * sizeof(bf16)) +
-         n_qtiles * sizeof(int);
+  size_t n = align256((size_t)Hkv * D * transpose_perm16_padded_len(Sk) * sizeof(bf16)) +
+             align256(n_qtiles * sizeof(int));
+  const int ks = fwd_ksplit(Sq, Sk, Hq);
+  if (ks > 1) {
+    const size_t slots = (size_t)Hq * (size_t)((Sq + 255) / 256) * ks;
+    n += align256(slots * 256 * HD * sizeof(float)) + align256(slots * 256 * sizeof(float));
+  }
+  return n;
 }
 
 void attn_fwd_workspace_layout(AttnArgs& a, void* base) {
   char* p = reinterpret_cast<char*>(base);
   a.vt = p;
   a.vt_ld = transpose_perm16_padded_len(a.Sk);
-  a.q_order = reinterpret_cast<int*>(p + align256((size_t)a.Hkv * a.D * a.vt_ld * sizeof(bf16)));
+  p += align256((size_t)a.Hkv * a.D * a.vt_ld * sizeof(bf16));
+  a.q_order = reinterpret_cast<int*>(p);
+  p += align256((size_t)((a.Sq + 127) / 128) * sizeof(int));
+  a.ksplit = fwd_ksplit(a.Sq, a.Sk, a.Hq);
+  if (a.ksplit > 1) {
+    const size_t slots = (size_t)a.Hq * (size_t)((a.Sq + 255) / 256) * a.ksplit;
+    a.o_part = reinterpret_cast<float*>(p);
+    p += align256(slots * 256 * HD * sizeof(float));
+    a.lse_part = reinterpret_cast<float*>(p);
+  }
 }
 
 namespace {
-template <int NW>
+template <int NW, bool SPLIT>
 hipError_t launch_fwd_nw(const AttnArgs& a, int o_f32, hipStream_t stream) {
   constexpr int BR = 32 * NW;
   const int n_qtiles = (a.Sq + BR - 1) / BR;
   hipError_t e = launch_schedule_q_tiles(a, n_qtiles, BR, a.q_order, stream);
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)(((n_qtiles + NXCD - 1) / NXCD) * NXCD * a.Hq));
+  const int nch = SPLIT ? a.ksplit : 1;
+  dim3 grid((unsigned)(((n_qtiles + NXCD - 1) / NXCD) * NXCD * a.Hq * nch));
   if (o_f32)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<true, NW>), grid, dim3(NW * 64), 0, stream, a, n_qtiles);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<true, NW, SPLIT>), grid, dim3(NW * 64), 0, stream, a, n_qtiles);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, NW>), grid, dim3(NW * 64), 0, stream, a, n_qtiles);
-  return hipGetLastError();
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, NW, SPLIT>), grid, dim3(NW * 64), 0, stream, a, n_qtiles);
+  e = hipGetLastError();
+  if constexpr (SPLIT) {
+    if (e != hipSuccess) return e;
+    const int64_t threads = (int64_t)a.Hq * a.Sq * 16;
+    dim3 cgrid((unsigned)((threads + 255) / 256));
+    if (o_f32)
+      hipLaunchKernelGGL((attn_fwd_combine_kernel<true, BR>), cgrid, dim3(256), 0, stream, a, n_qtiles);
+    else
+      hipLaunchKernelGGL((attn_fwd_combine_kernel<false, BR>), cgrid, dim3(256), 0, stream, a, n_qtiles);
+    e = hipGetLastError();
+  }
+  return e;
 }
 }  // namespace
 
@@ -354,16 +453,18 @@ int device_cu_count() {
   return n;
 }
 
-// a.vt must point at a workspace of attn_fwd_workspace_bytes; it is filled here.
+// a.vt must point at a workspace of attn_fwd_workspace_bytes (laid out by
+// attn_fwd_workspace_layout); V^T is filled here.
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t stream) {
   if (a.Sq == 0) return hipSuccess;
   if (a.Sk > 0) {
     hipError_t e = launch_transpose_perm16(a.v, a.lk, a.Sk, a.Hkv, const_cast<void*>(a.vt), stream);
     if (e != hipSuccess) return e;
   }
+  if (a.ksplit > 1) return launch_fwd_nw<8, true>(a, o_f32, stream);
   const int64_t wg256 = (int64_t)((a.Sq + 255) / 256) * a.Hq;
-  if (wg256 < device_cu_count()) return launch_fwd_nw<4>(a, o_f32, stream);
-  return launch_fwd_nw<8>(a, o_f32, stream);
+  if (wg256 < device_cu_count()) return launch_fwd_nw<4, false>(a, o_f32, stream);
+  return launch_fwd_nw<8, false>(a, o_f32, stream);
 }
 
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream) {

@@ -94,6 +94,13 @@ struct AttnArgs {
   const void* vt;      // bf16 path: V in head-dim-major layout (see transpose.hip)
   int64_t vt_ld;       // its padded token length
   int* q_order;        // bf16 path: query tiles heaviest first (schedule.hip)
+  // bf16 forward with split key ranges (ksplit > 1): each query tile's visible keys
+  // are cut into ksplit chunks, one workgroup each, whose normalised partial O and
+  // LSE go to o_part [Hq][tiles][ksplit][256][128] and lse_part [Hq][tiles][ksplit][256]
+  // (fp32) before a combine pass
+  int ksplit;
+  float* o_part;
+  float* lse_part;
   RowLayout lq;        // bf16 path: rows of q, o (and of dout, dq in the backward)
   RowLayout lk;        // bf16 path: rows of k, v (and of dk, dv)
 };
@@ -147,7 +154,7 @@ __device__ __forceinline__ int first_row_seeing(const AttnArgs& a, int j) {
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t s);
 int device_cu_count();
-size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hkv, int32_t D, int bf16_path);
+size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D, int bf16_path);
 // fills a.vt, a.vt_ld and a.q_order from the workspace base (bf16 path)
 void attn_fwd_workspace_layout(AttnArgs& a, void* base);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t s);

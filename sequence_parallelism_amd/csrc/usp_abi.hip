@@ -67,6 +67,9 @@ AttnArgs make_args(const void* q, const void* k, const void* v, int64_t Sq, int6
   a.vt = nullptr;
   a.vt_ld = 0;
   a.q_order = nullptr;
+  a.ksplit = 1;
+  a.o_part = nullptr;
+  a.lse_part = nullptr;
   a.lq = contiguous_rows(Hq);
   a.lk = contiguous_rows(Hkv);
   return a;
@@ -88,7 +91,7 @@ usp_status attn_fwd_impl(const void* q, const void* k, const void* v, int64_t Sq
   if (st != USP_OK) return st;
   if (bad_dtype(o_dtype) || (in_dtype == USP_F32 && o_dtype != USP_F32)) return USP_ERR_BAD_DTYPE;
   if (o_dtype == USP_F32 && !aligned(o, 16) && in_dtype == USP_BF16) return USP_ERR_MISALIGNED;
-  const size_t need = attn_fwd_workspace_bytes(Sq, Sk, Hkv, D, in_dtype == USP_BF16);
+  const size_t need = attn_fwd_workspace_bytes(Sq, Sk, Hq, Hkv, D, in_dtype == USP_BF16);
   if (need > 0 && !workspace) return USP_ERR_NULL_POINTER;
   if (workspace && !aligned(workspace, 16)) return USP_ERR_MISALIGNED;
   if (workspace_bytes < need) return USP_ERR_WORKSPACE_TOO_SMALL;
@@ -177,7 +180,7 @@ usp_status blockattn_fwd_workspace_size(int64_t Sq, int64_t Sk, int32_t Hq, int3
   if (!bytes) return USP_ERR_NULL_POINTER;
   if (bad_dtype(in_dtype)) return USP_ERR_BAD_DTYPE;
   if (Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1) return USP_ERR_BAD_SHAPE;
-  *bytes = attn_fwd_workspace_bytes(Sq, Sk, Hkv, D, in_dtype == USP_BF16);
+  *bytes = attn_fwd_workspace_bytes(Sq, Sk, Hq, Hkv, D, in_dtype == USP_BF16);
   return USP_OK;
 }
 
@@ -276,7 +279,7 @@ usp_status usp_ulysses_attn_fwd(const void* xq, const void* xk, const void* xv, 
   usp_status st = ulysses_args(xq, xk, xv, P, S_local, Hq_total, Hkv_total, D, group, position_ids,
                                causal, softmax_scale, in_dtype, o_seq, lse, lse_ld, &a);
   if (st != USP_OK) return st;
-  const size_t need = attn_fwd_workspace_bytes(a.Sq, a.Sk, a.Hkv, D, 1);
+  const size_t need = attn_fwd_workspace_bytes(a.Sq, a.Sk, a.Hq, a.Hkv, D, 1);
   if (!workspace) return USP_ERR_NULL_POINTER;
   if (!aligned(workspace, 16)) return USP_ERR_MISALIGNED;
   if (workspace_bytes < need) return USP_ERR_WORKSPACE_TOO_SMALL;
