@@ -31,6 +31,8 @@
 // document starts).  Fully visible tiles run first, without any masking work; the
 // few boundary tiles (the causal diagonal, a document boundary, a partial tile)
 // run after them with the mask folded into the row log-sum-exp.
+#include <algorithm>
+
 #include "gfx950.h"
 
 namespace {
@@ -86,6 +88,9 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
 }
 
 // ---- 3. main ----------------------------------------------------------------------
+// SPLIT: the workgroup takes chunk c of its key block's items (a.kv_split chunks) and
+// writes its partial dK^T, dV^T sums for the combine pass.
+template <bool SPLIT>
 __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, int n_qtiles) {
   // per buffer: Q [64 rows][128], dO [64][128] (swz16), Q^T [128][64 positions],
   // dO^T [128][64] (swz8) -- 4 tiles of 16 KB
@@ -99,10 +104,14 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, hi = lane >> 5;
-  // key blocks start heaviest first (schedule.hip); heads of one block are adjacent
+  // key blocks start heaviest first (schedule.hip); heads of one block are adjacent,
+  // then the chunks of a split block
   const int hk = blockIdx.x % f.Hkv;
+  const int nch = SPLIT ? a.kv_split : 1;
+  const int chunk = SPLIT ? (blockIdx.x / f.Hkv) % nch : 0;
   const int n_kb = (f.Sk + BKV - 1) / BKV;              // the order is a permutation of [0, n_kb)
-  const int k0 = min(max(a.kv_order[blockIdx.x / f.Hkv], 0), n_kb - 1) * BKV;   // first key
+  const int kbi = min(max(a.kv_order[blockIdx.x / f.Hkv / nch], 0), n_kb - 1);
+  const int k0 = kbi * BKV;                             // first key
   const int kw0 = k0 + wave * 32;                       // this wave's first key
   const int kl = kw0 + r32;                             // this lane's key (B-operand column)
   const bool key_ok = kl < f.Sk;
@@ -174,6 +183,9 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   const int first_masked = t0 < m1 ? t0 : m2;
   const int n_full = grp * (f1 - f0);
   const int n_items = n_full + grp * ((m1 - t0) + (t1 - m2));
+  // this workgroup's items [it0, it1): all of them, or chunk `chunk` of a split block
+  const int it0 = SPLIT ? (int)((int64_t)chunk * n_items / nch) : 0;
+  const int it1 = SPLIT ? (int)((int64_t)(chunk + 1) * n_items / nch) : n_items;
 
   // ---- staging of one item by LDS-DMA ------------------------------------------------
   // Tile u (Q, dO, Q^T, dO^T) is 1024 16-byte chunks; wave w, load i covers physical
@@ -306,12 +318,26 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   // item 0 is staged before the loop; nx: where item it+1 comes from (used by item
   // it), worked out during item it-1; (h2, t2): item it+2 (the last item repeats
   // itself past the end)
-  int h2 = hk * grp, t2 = n_full > 0 ? f0 : first_masked;
+  // (h, t) of item `it` in the visiting order (next_item steps through it)
+  auto item_at = [&](int it, int& h, int& t) {
+    if (it < n_full) {
+      const int nf = f1 - f0;
+      h = hk * grp + it / nf;
+      t = f0 + it % nf;
+    } else {
+      const int i2 = it - n_full, na = m1 - t0, nm = na + (t1 - m2);
+      h = hk * grp + i2 / nm;
+      const int x = i2 % nm;
+      t = x < na ? t0 + x : m2 + (x - na);
+    }
+  };
+  int h2 = hk * grp, t2 = first_masked;
+  if (it0 < it1) item_at(it0, h2, t2);
   const ItemSrc src0 = item_src(h2, t2);
-  if (n_items > 1) next_item(h2, t2);
+  if (it1 - it0 > 1) next_item(h2, t2);
   ItemSrc nx = item_src(h2, t2);
-  if (n_items > 2) next_item(h2, t2);
-  if (n_items > 0) {
+  if (it1 - it0 > 2) next_item(h2, t2);
+  if (it0 < it1) {
     uint32_t vq = 0;
     for (int j = 0; j < 16; ++j) dma_step(j, src0, 0, vq);
     load_scalars(src0);
@@ -326,7 +352,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   // log-sum-exp +inf so that P and dS vanish there
   auto run_item = [&](auto mask_tag, int it) {
     constexpr bool MASK = decltype(mask_tag)::v != 0;
-    const int buf = it & 1;
+    const int buf = (it - it0) & 1;
     ItemSrc nx2;
     // every wave is done with item it-1, which read buffer buf ^ 1: it can be refilled
     // (item it itself was published halfway through item it-1's last slot)
@@ -442,15 +468,34 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
     }
 
     nx = nx2;
-    if (it + 3 < n_items) next_item(h2, t2);
+    if (it + 3 < it1) next_item(h2, t2);
   };
 #pragma unroll 1
-  for (int it = 0; it < n_full; ++it) run_item(IC<0>{}, it);
+  for (int it = it0; it < min(it1, n_full); ++it) run_item(IC<0>{}, it);
 #pragma unroll 1
-  for (int it = n_full; it < n_items; ++it) run_item(IC<1>{}, it);
+  for (int it = max(it0, n_full); it < it1; ++it) run_item(IC<1>{}, it);
   // the last accumulations (inline-assembly MFMAs) complete before any read below
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   // ---- dK = scale dK^T, dV = dV^T (bf16), lane: key kl, d = 32db + 8g4 + 4hi + 0..3
+  if (SPLIT) {   // the chunk's partial sums, unscaled
+    if (key_ok) {
+      const int64_t slot = ((int64_t)hk * n_kb + kbi) * nch + chunk;
+      float* dkp = a.kv_part + ((slot * 2 + 0) * BKV + (kl - k0)) * HD;
+      float* dvp = a.kv_part + ((slot * 2 + 1) * BKV + (kl - k0)) * HD;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = 32 * db + 8 * g4 + 4 * hi;
+          *reinterpret_cast<f32x4*>(dkp + d) =
+              f32x4{dka[db][4 * g4], dka[db][4 * g4 + 1], dka[db][4 * g4 + 2], dka[db][4 * g4 + 3]};
+          *reinterpret_cast<f32x4*>(dvp + d) =
+              f32x4{dva[db][4 * g4], dva[db][4 * g4 + 1], dva[db][4 * g4 + 2], dva[db][4 * g4 + 3]};
+        }
+      }
+    }
+    return;
+  }
   if (key_ok) {
     const int64_t base = rows_off(f.lk, kl, hk);
     bf16* dkp = reinterpret_cast<bf16*>(a.dk) + base;
@@ -471,6 +516,37 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   }
 }
 
+// dK = scale * (sum of the chunk partials), dV = sum, bf16; 16 lanes per (head, key)
+__global__ __launch_bounds__(256) void attn_bwd_kv_combine_kernel(AttnBwdArgs a) {
+  const AttnArgs& f = a.f;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rid = gid >> 4;
+  const int sub = threadIdx.x & 15;
+  if (rid >= (int64_t)f.Hkv * f.Sk) return;
+  const int hk = (int)(rid / f.Sk), key = (int)(rid - (int64_t)hk * f.Sk);
+  const int n_kb = (f.Sk + BKV - 1) / BKV;
+  const int kbi = key / BKV, kr = key - kbi * BKV;
+  const int64_t slot0 = ((int64_t)hk * n_kb + kbi) * a.kv_split;
+  float dk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, dv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < a.kv_split; ++c) {
+    const float* pk = a.kv_part + (((slot0 + c) * 2 + 0) * BKV + kr) * HD + 8 * sub;
+    const float* pv = a.kv_part + (((slot0 + c) * 2 + 1) * BKV + kr) * HD + 8 * sub;
+    const f32x4 k0 = *reinterpret_cast<const f32x4*>(pk), k1 = *reinterpret_cast<const f32x4*>(pk + 4);
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(pv), v1 = *reinterpret_cast<const f32x4*>(pv + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dk[e] += k0[e]; dk[4 + e] += k1[e];
+      dv[e] += v0[e]; dv[4 + e] += v1[e];
+    }
+  }
+  bf16x8 ok, ov;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { ok[e] = (bf16)(dk[e] * f.scale); ov[e] = (bf16)dv[e]; }
+  const int64_t off = rows_off(f.lk, key, hk) + 8 * sub;
+  *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.dk) + off) = ok;
+  *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.dv) + off) = ov;
+}
+
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 size_t n_kv_blocks(int64_t Sk) { return (size_t)((Sk + BKV - 1) / BKV); }
 size_t n_dq_tiles(int64_t Sq) {
@@ -480,14 +556,28 @@ size_t n_dq_tiles(int64_t Sq) {
 
 }  // namespace
 
+// Item-range split of the dK/dV kernel for a call: 1 (none) unless its key blocks
+// (times key/value heads) give at most two workgroups per CU and its query tiles are
+// many; then chunks for about four workgroups per CU, at most 8.
+int bwd_kv_split(int64_t Sq, int64_t Sk, int32_t Hkv) {
+  const int64_t wg = (int64_t)n_kv_blocks(Sk) * Hkv;
+  const int cus = device_cu_count();
+  if (wg == 0 || wg > 2 * (int64_t)cus || Sq < 2048) return 1;
+  return (int)std::min<int64_t>(8, (4 * (int64_t)cus + wg - 1) / wg);
+}
+
 size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D) {
   const size_t sq_pad = (size_t)transpose_perm16_padded_len(Sq);
   const size_t sk_pad = (size_t)transpose_perm16_padded_len(Sk);
-  return align256((size_t)Sq * Hq * sizeof(float))                       // D
-         + 2 * align256((size_t)Hq * D * sq_pad * sizeof(bf16))           // q^T, dout^T
-         + align256((size_t)Hkv * D * sk_pad * sizeof(bf16))              // k^T
-         + align256(n_kv_blocks(Sk) * sizeof(int))                        // key-block order
-         + n_dq_tiles(Sq) * sizeof(int);                                  // dQ tile order
+  size_t n = align256((size_t)Sq * Hq * sizeof(float))                       // D
+             + 2 * align256((size_t)Hq * D * sq_pad * sizeof(bf16))           // q^T, dout^T
+             + align256((size_t)Hkv * D * sk_pad * sizeof(bf16))              // k^T
+             + align256(n_kv_blocks(Sk) * sizeof(int))                        // key-block order
+             + align256(n_dq_tiles(Sq) * sizeof(int));                        // dQ tile order
+  const int qs = bwd_dq_split(Sq, Sk, Hq), ks = bwd_kv_split(Sq, Sk, Hkv);
+  if (qs > 1) n += align256((size_t)Hq * (size_t)((Sq + 255) / 256) * qs * 256 * HD * sizeof(float));
+  if (ks > 1) n += align256((size_t)Hkv * n_kv_blocks(Sk) * ks * 2 * BKV * HD * sizeof(float));
+  return n;
 }
 
 void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
@@ -506,6 +596,16 @@ void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
   a.kv_order = reinterpret_cast<int*>(p);
   p += align256(n_kv_blocks(f.Sk) * sizeof(int));
   a.dq_order = reinterpret_cast<int*>(p);
+  p += align256(n_dq_tiles(f.Sq) * sizeof(int));
+  a.dq_split = bwd_dq_split(f.Sq, f.Sk, f.Hq);
+  a.kv_split = bwd_kv_split(f.Sq, f.Sk, f.Hkv);
+  a.dq_part = nullptr;
+  a.kv_part = nullptr;
+  if (a.dq_split > 1) {
+    a.dq_part = reinterpret_cast<float*>(p);
+    p += align256((size_t)f.Hq * (size_t)((f.Sq + 255) / 256) * a.dq_split * 256 * HD * sizeof(float));
+  }
+  if (a.kv_split > 1) a.kv_part = reinterpret_cast<float*>(p);
 }
 
 bool attn_bwd_supported(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv) {
@@ -534,8 +634,20 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
     const int n_qtiles = (f.Sq + BQ - 1) / BQ;
     e = launch_schedule_kv_blocks(f, n_ktiles, BKV, BQ, a.kv_order, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_bwd_main_kernel, dim3((unsigned)(n_ktiles * f.Hkv)), dim3(NWB * 64), 0,
-                       stream, a, n_qtiles);
+    if (a.kv_split > 1) {
+      hipLaunchKernelGGL(attn_bwd_main_kernel<true>, dim3((unsigned)(n_ktiles * f.Hkv * a.kv_split)),
+                         dim3(NWB * 64), 0, stream, a, n_qtiles);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t threads = (int64_t)f.Hkv * f.Sk * 16;
+      hipLaunchKernelGGL(attn_bwd_kv_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                         stream, a);
+    } else {
+      hipLaunchKernelGGL(attn_bwd_main_kernel<false>, dim3((unsigned)(n_ktiles * f.Hkv)), dim3(NWB * 64), 0,
+                         stream, a, n_qtiles);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   return launch_attn_bwd_dq(a, stream);
 }

@@ -19,6 +19,8 @@
 //   * tiles fully visible to a wave skip the per-element mask;
 //   * a wave raises its priority (s_setprio) while it issues MFMAs, so the other
 //     wave of its SIMD overlaps its softmax with them.
+#include <algorithm>
+
 #include "gfx950.h"
 
 namespace {
@@ -33,7 +35,9 @@ constexpr int NXCD = 8;          // MI355X dispatches workgroup i to XCD i % 8
 
 // NW wavefronts (32 query rows each) per workgroup: 8 normally, 4 when a call has
 // too few 256-row tiles to give every CU a workgroup.
-template <int NW>
+// SPLIT: the workgroup takes chunk c of its tile's key range (a.dq_split chunks) and
+// writes its partial dQ^T sum for the combine pass.
+template <int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int n_qtiles) {
   constexpr int BR = 32 * NW;              // query rows per workgroup
   constexpr int NL = TILE / 8 / (NW * 64); // 64-lane DMA loads per wave per staged tile
@@ -51,7 +55,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   // work (schedule.hip)
   const int xcd = blockIdx.x % NXCD, j = blockIdx.x / NXCD;
   const int h = j % f.Hq;
-  const int rank = (j / f.Hq) * NXCD + xcd;
+  const int nch = SPLIT ? a.dq_split : 1;
+  const int chunk = SPLIT ? (j / f.Hq) % nch : 0;
+  const int rank = (j / f.Hq / nch) * NXCD + xcd;
   if (rank >= n_qtiles) return;                             // grid padding (whole workgroup)
   const int qt = min(max(a.dq_order[rank], 0), n_qtiles - 1);   // a permutation of the tiles
   const int hk = h / (f.Hq / f.Hkv);
@@ -70,8 +76,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   g_hiex = __builtin_amdgcn_readfirstlane(g_hiex);
   // local key range [kb, ke); tiles start on 64-key boundaries (inside one block of
   // the key layout, and on the 16-key groups of the K^T slot order)
-  const int ke = g_hiex;
-  const int kb = g_lo & ~(BC - 1);
+  int ke = g_hiex;
+  int kb = g_lo & ~(BC - 1);
+  if (SPLIT) {   // chunk `chunk` of [kb, ke): equal lengths, multiples of the tile
+    const int len = ((ke > kb ? ceil_div(ke - kb, nch) : 0) + BC - 1) & ~(BC - 1);
+    kb += chunk * len;
+    ke = min(ke, kb + len);
+  }
 
   // ---- Q and dO fragments (B operands of S^T = K Q^T, dP^T = V dO^T):
   // row r32, d = 16 kk + 8 hi + 0..7 ------------------------------------------------
@@ -222,6 +233,22 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   }
 
   // ---- epilogue: dQ = scale dQ^T (bf16); lane: row r32, d = 32 db + 8 g4 + 4 hi + 0..3
+  if (SPLIT) {   // the chunk's partial sum, unscaled
+    if (row_ok) {
+      const int64_t slot = ((int64_t)h * n_qtiles + qt) * nch + chunk;
+      float* dst = a.dq_part + (slot * BR + wave * 32 + r32) * HD;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = 32 * db + 8 * g4 + 4 * hi;
+          *reinterpret_cast<f32x4*>(dst + d) = f32x4{dqacc[db][4 * g4], dqacc[db][4 * g4 + 1],
+                                                     dqacc[db][4 * g4 + 2], dqacc[db][4 * g4 + 3]};
+        }
+      }
+    }
+    return;
+  }
   if (row_ok) {
     bf16* dqp = reinterpret_cast<bf16*>(a.dq) + rows_off(f.lq, row, h);
 #pragma unroll
@@ -237,6 +264,31 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   }
 }
 
+// dQ = scale * (sum of the chunk partials), bf16, per (head, row); 16 lanes per row
+template <int BR>
+__global__ __launch_bounds__(256) void attn_bwd_dq_combine_kernel(AttnBwdArgs a, int n_qtiles) {
+  const AttnArgs& f = a.f;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rid = gid >> 4;
+  const int sub = threadIdx.x & 15;
+  if (rid >= (int64_t)f.Hq * f.Sq) return;
+  const int h = (int)(rid / f.Sq), row = (int)(rid - (int64_t)h * f.Sq);
+  const int qt = row / BR, rr = row - qt * BR;
+  const int64_t slot0 = ((int64_t)h * n_qtiles + qt) * a.dq_split;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < a.dq_split; ++c) {
+    const float* src = a.dq_part + ((slot0 + c) * BR + rr) * HD + 8 * sub;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { acc[e] += x0[e]; acc[4 + e] += x1[e]; }
+  }
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (bf16)(acc[e] * f.scale);
+  *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.dq) + rows_off(f.lq, row, h) + 8 * sub) = v;
+}
+
 }  // namespace
 
 // a must carry the workspace regions of attn_bwd_workspace_layout, with D and the
@@ -245,23 +297,41 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
 int attn_bwd_dq_rows_per_tile() { return 128; }
 
 namespace {
-template <int NW>
+template <int NW, bool SPLIT>
 hipError_t launch_dq_nw(const AttnBwdArgs& a, hipStream_t stream) {
   constexpr int BR = 32 * NW;
   const AttnArgs& f = a.f;
   const int n_qtiles = (f.Sq + BR - 1) / BR;
   hipError_t e = launch_schedule_q_tiles(f, n_qtiles, BR, a.dq_order, stream);
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)(((n_qtiles + NXCD - 1) / NXCD) * NXCD * f.Hq));
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<NW>), grid, dim3(NW * 64), 0, stream, a, n_qtiles);
-  return hipGetLastError();
+  const int nch = SPLIT ? a.dq_split : 1;
+  dim3 grid((unsigned)(((n_qtiles + NXCD - 1) / NXCD) * NXCD * f.Hq * nch));
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<NW, SPLIT>), grid, dim3(NW * 64), 0, stream, a, n_qtiles);
+  e = hipGetLastError();
+  if constexpr (SPLIT) {
+    if (e != hipSuccess) return e;
+    const int64_t threads = (int64_t)f.Hq * f.Sq * 16;
+    hipLaunchKernelGGL((attn_bwd_dq_combine_kernel<BR>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, a, n_qtiles);
+    e = hipGetLastError();
+  }
+  return e;
 }
 }  // namespace
+
+// Key-range split of the dQ kernel for a call: as the forward's (fwd_ksplit).
+int bwd_dq_split(int64_t Sq, int64_t Sk, int32_t Hq) {
+  const int64_t wg = (int64_t)((Sq + 255) / 256) * Hq;
+  const int cus = device_cu_count();
+  if (wg == 0 || wg >= cus || Sk < 2048) return 1;
+  return (int)std::min<int64_t>(16, (4 * (int64_t)cus + wg - 1) / wg);
+}
 
 hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, hipStream_t stream) {
   const AttnArgs& f = a.f;
   if (f.Sq == 0) return hipSuccess;
+  if (a.dq_split > 1) return launch_dq_nw<8, true>(a, stream);
   const int64_t wg256 = (int64_t)((f.Sq + 255) / 256) * f.Hq;
-  if (wg256 < device_cu_count()) return launch_dq_nw<4>(a, stream);
-  return launch_dq_nw<8>(a, stream);
+  if (wg256 < device_cu_count()) return launch_dq_nw<4, false>(a, stream);
+  return launch_dq_nw<8, false>(a, stream);
 }

@@ -173,7 +173,18 @@ struct AttnBwdArgs {
   int* kv_order;       // key blocks of the dK/dV kernel, heaviest first
   int* dq_order;       // query tiles of the dQ kernel, heaviest first
   int64_t sq_pad, sk_pad;
+  // split key ranges of the dQ kernel (dq_split > 1): partial dQ^T sums per chunk,
+  // dq_part [Hq][tiles][dq_split][256][128] fp32, summed by a combine pass
+  int dq_split;
+  float* dq_part;
+  // split query-tile ranges of the dK/dV kernel (kv_split > 1): partial dK^T, dV^T
+  // sums per chunk, kv_part [Hkv][key blocks][kv_split][2][128 keys][128] fp32
+  int kv_split;
+  float* kv_part;
 };
+// key-range / item-range splits of the backward kernels for a call's sizes (1: none)
+int bwd_dq_split(int64_t Sq, int64_t Sk, int32_t Hq);
+int bwd_kv_split(int64_t Sq, int64_t Sk, int32_t Hkv);
 size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D);
 // fills the workspace pointers of a from its base (layout of attn_bwd_workspace_bytes)
 void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base);
