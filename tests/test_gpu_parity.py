@@ -297,3 +297,38 @@ def test_lse_merge_random(usp, adt, pdt, D):
     rel = 1e-6 if adt == torch.float32 else 2.0 ** -8
     assert np.all(np.abs(f64(oad) - ref_o) <= 1e-5 + rel * np.abs(ref_o))
     check_lse(lad, ref_l, "merge lse")
+
+
+# ---- split key / query ranges (calls too small to fill the GPU with whole tiles) ---------
+
+@pytest.mark.parametrize("S,Hq,Hkv,lengths,causal", [
+    (3000, 4, 2, None, True),                     # ragged tail, GQA 2:1: 16 chunks per tile
+    (2500, 2, 1, None, False),                    # non-causal
+    (4200, 2, 2, [1500, 1, 2000, 699], True),     # packed docs incl. a 1-token doc
+    (2048, 1, 1, [2048], True),                   # the smallest split call
+])
+def test_split_paths_fwd_bwd(usp, S, Hq, Hkv, lengths, causal):
+    """Sizes whose 256-row tiles leave CUs idle: the forward and dQ kernels split key
+    ranges, the dK/dV kernel splits query-tile ranges, and combine passes merge the
+    partials; checked against the oracle over the whole sequence."""
+    say("split paths", S, Hq, Hkv, causal)
+    q, k, v, do, pos = inputs.attention_case(S, Hq, Hkv, 128, seed=41, lengths=lengths)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    posd = torch.from_numpy(pos).to(DEV) if causal else None
+    o, lse = usp.blockattn_fwd(qd, kd, vd, posd, causal=causal)
+    dq, dk, dv = usp.blockattn_bwd(qd, kd, vd, o, lse, dod, posd, causal=causal)
+    torch.cuda.synchronize()
+    kw = dict(pos=pos, causal=True) if causal else dict(causal=False)
+    args = (f64(q), f64(k), f64(v))
+    ref_o, ref_l = oracle.attention_fwd(*args, **kw)
+    check_o(o.cpu(), ref_o, "o")
+    check_lse(lse.cpu(), ref_l, "lse")
+    rq, rk, rv = oracle.attention_bwd(*args, f64(do), **kw)
+    check_grad(dq.cpu(), rq, "dq")
+    check_grad(dk.cpu(), rk, "dk")
+    check_grad(dv.cpu(), rv, "dv")
+    # fp32 partial output (the ring's o_dtype) through the same split path
+    o32, lse32 = usp.blockattn_fwd(qd, kd, vd, posd, causal=causal, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_o(o32.cpu(), ref_o, "o fp32")
+    assert torch.equal(lse32, lse)
