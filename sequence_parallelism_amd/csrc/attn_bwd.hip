@@ -7,16 +7,17 @@
 //
 // Kernels, in stream order:
 //   1. pre:       D_i for every (row, head);
-//   2. transpose: head-dim-major copies of q, dout and k in the workspace
-//                 (transpose.hip), so that every MFMA operand read from LDS below
-//                 is ONE 16-byte read (narrower LDS reads cost as much issue time
-//                 as 16-byte ones on gfx950);
+//   2. transpose: the head-dim-major copy of k in the workspace (transpose.hip) for
+//                 the dQ kernel;
 //   3. dK, dV:    a workgroup owns 128 keys of one key/value head (32 per wave; K
 //                 and V of the lane's key are B operands in registers) and walks the
 //                 64-row query tiles that can see the block, for every query head of
 //                 the group (one "item" = one (head, tile) pair).  An item is Q and
-//                 dO row-major plus Q^T and dO^T head-dim-major (64 KB), brought into
-//                 double-buffered LDS by LDS-DMA one item ahead.  Per item each wave
+//                 dO row-major (32 KB), brought into double-buffered LDS by LDS-DMA
+//                 one item ahead; the operands of dV^T and dK^T, which need Q and dO
+//                 transposed, are read from the same tiles with the transposing LDS
+//                 read (two 8-byte reads per operand cost about as much as one
+//                 16-byte read).  Per item each wave
 //                 runs one software pipeline of 64 MFMAs (v_mfma_f32_32x32x16_bf16,
 //                 one key per lane, 16 rows per lane):
 //                   S, dP of rows 0-31 | S, dP of rows 32-63 | dV^T, dK^T of rows
@@ -92,9 +93,8 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
 // writes its partial dK^T, dV^T sums for the combine pass.
 template <bool SPLIT>
 __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, int n_qtiles) {
-  // per buffer: Q [64 rows][128], dO [64][128] (swz16), Q^T [128][64 positions],
-  // dO^T [128][64] (swz8) -- 4 tiles of 16 KB
-  __shared__ __attribute__((aligned(16))) bf16 stage[2][4 * TILE];
+  // per buffer: Q [64 rows][128], dO [64][128] (swz16) -- 2 tiles of 16 KB
+  __shared__ __attribute__((aligned(16))) bf16 stage[2][2 * TILE];
   __shared__ __attribute__((aligned(16))) float lse2_s[2][BQ];
   __shared__ __attribute__((aligned(16))) float ndelta_s[2][BQ];   // -D
   __shared__ __attribute__((aligned(16))) int klo_s[2][BQ];   // visible keys [klo, khi)
@@ -144,7 +144,22 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   //   Q / dO row reads (A operands of S, dP): row r32 (+32 qb), chunks 2kk + hi
   //   Q^T / dO^T reads (A operands of dV^T, dK^T): row r32 (+32 db), chunks 2c + hi
   const int qbase = r32 * HD + ((hi ^ swz16(r32)) << 3);
-  const int tbase = r32 * BQ + ((hi ^ swz8(r32)) << 3);
+  //   Q / dO transposed reads (A operands of dV^T, dK^T: head-dim row d = r32 + 32db,
+  //   reduction slots = rows 16c + 8(s/4) + 4hi + s%4): in 16-lane group g, lane s
+  //   names row 16c + 8half + 4(g/2) + s/4 at columns 32db + 16(g%2) + 4(s%4).  The
+  //   row's swizzle is swz16(row in the group) ^ 2half, and db flips chunk bits 2-3,
+  //   so the byte offset is  (tr0 ^ 64db ^ 32half) + (16c + 8half) * 256.
+  uint32_t tr_off[4][2];
+  {
+    const int g = lane >> 4, s = lane & 15;
+    const int row = 4 * (g >> 1) + (s >> 2), col = 16 * (g & 1) + 4 * (s & 3);
+    const uint32_t tr0 = (uint32_t)(row * HD * 2 + (((col >> 3) ^ swz16(row)) << 4) + (col & 7) * 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      tr_off[db][0] = tr0 ^ (uint32_t)(64 * db);
+      tr_off[db][1] = (tr0 ^ (uint32_t)(64 * db + 32)) + 8 * HD * 2;
+    }
+  }
 
   // ---- query tiles that can see the block: [t0, t1) ------------------------------
   // and among them the fully visible ones [f0, f1): every row valid, every key of
@@ -188,17 +203,12 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   const int it1 = SPLIT ? (int)((int64_t)(chunk + 1) * n_items / nch) : n_items;
 
   // ---- staging of one item by LDS-DMA ------------------------------------------------
-  // Tile u (Q, dO, Q^T, dO^T) is 1024 16-byte chunks; wave w, load i covers physical
-  // chunks [(4i + w) * 64, +64), lane l the chunk (4i + w) * 64 + l, i.e.
-  //   Q, dO:     row 16i + 4w + l/16, physical chunk l%16;
-  //   Q^T, dO^T: head-dim row 32i + 8w + l/8, physical chunk l%8.
-  // Row and chunk of load i differ from load 0's by 16i rows (Q, dO) or 32i head-dim
-  // rows (Q^T, dO^T); the swizzle depends on the row modulo 16 only, so one lane
-  // offset each suffices (the 32i-row step of Q^T, dO^T goes into the uniform base).
+  // Tile u (Q, dO) is 1024 16-byte chunks; wave w, load i covers physical chunks
+  // [(4i + w) * 64, +64), lane l the chunk (4i + w) * 64 + l, i.e. row 16i + 4w + l/16,
+  // physical chunk l%16.  Load i's rows are load 0's plus 16i; the swizzle depends on
+  // the row modulo 16 only, so one lane offset suffices.
   const uint32_t rq_row = (uint32_t)(4 * wave + (lane >> 4));
   const uint32_t rq_lc = (uint32_t)((((lane & 15) ^ swz16(rq_row)) << 3) * 2);
-  const int rt_d = 8 * wave + (lane >> 3);
-  const uint32_t rt_off = (uint32_t)((rt_d * a.sq_pad + (((lane & 7) ^ swz8(rt_d)) << 3)) * 2);
   const uint32_t rowqB = (uint32_t)f.lq.row_stride * 2;           // bytes per q / dout row
   const uint32_t stage_lds = lds_addr(&stage[0][0]);
 
@@ -207,7 +217,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   // the first MFMAs of the item that issues it): the four tiles' sources, the row
   // clamp, and this lane's row-scalar addresses.
   struct ItemSrc {
-    const char* tile[4];   // Q, dO rows q0.. ; Q^T, dO^T columns q0..
+    const char* tile[2];   // Q, dO rows q0..
     uint32_t lim;          // rows past Sq are clamped to the last row (the mask zeroes them)
     int q0;
     const float* lse;
@@ -221,9 +231,6 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
     const int64_t rq = rows_off(f.lq, q0, h) * 2;
     r.tile[0] = reinterpret_cast<const char*>(f.q) + rq;
     r.tile[1] = reinterpret_cast<const char*>(a.dout) + rq;
-    const int64_t rt = ((int64_t)h * HD * a.sq_pad + q0) * 2;
-    r.tile[2] = reinterpret_cast<const char*>(a.qt) + rt;
-    r.tile[3] = reinterpret_cast<const char*>(a.dot) + rt;
     r.lim = (uint32_t)(f.Sq - 1 - q0);
     r.q0 = q0;
     const int row = min(q0 + lane, f.Sq - 1);
@@ -233,18 +240,13 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
     return r;
   };
 
-  // DMA j (0..15) of an item into buffer buf: load i = j/4 of tile u = j%4 (the
-  // head-dim-major tiles step 32 head-dim rows per load).  vq carries the clamped row
-  // offset from tile 0 to tile 1 of the same load.
+  // DMA j (0..7) of an item into buffer buf: load i = j/2 of tile u = j%2.  vq carries
+  // the clamped row offset from tile 0 to tile 1 of the same load.
   auto dma_step = [&](int j, const ItemSrc& src, int buf, uint32_t& vq) {
-    const int i = j >> 2, u = j & 3;
-    const uint32_t lds = stage_lds + (uint32_t)(((buf * 4 + u) * TILE + (4 * i + wave) * 512) * 2);
-    if (u < 2) {
-      if (u == 0) vq = min(rq_row + 16 * i, src.lim) * rowqB + rq_lc;
-      dma16(src.tile[u], vq, __builtin_amdgcn_readfirstlane(lds));
-    } else {
-      dma16(src.tile[u] + (int64_t)32 * i * a.sq_pad * 2, rt_off, __builtin_amdgcn_readfirstlane(lds));
-    }
+    const int i = j >> 1, u = j & 1;
+    const uint32_t lds = stage_lds + (uint32_t)(((buf * 2 + u) * TILE + (4 * i + wave) * 512) * 2);
+    if (u == 0) vq = min(rq_row + 16 * i, src.lim) * rowqB + rq_lc;
+    dma16(src.tile[u], vq, __builtin_amdgcn_readfirstlane(lds));
   };
 
   // Row scalars of an item, one row per lane, read one item ahead.  The reads are
@@ -301,10 +303,10 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
       constexpr int dp = sdp_order(j) >> 3, kk = sdp_order(j) & 7;
       const bf16* t = &stage[b][(dp ? 1 : 0) * TILE];
       return *reinterpret_cast<const bf16x8*>(&t[32 * slot * HD + (qbase ^ (16 * kk))]);
-    } else {                    // dV^T (even) / dK^T (odd), row chunk c, head-dim block db
+    } else {                    // dV^T (even: dO) / dK^T (odd: Q), row chunk c, head-dim block db
       constexpr int c = 2 * (slot - 2) + (j >> 3), db = (j >> 1) & 3;
-      const bf16* t = &stage[b][((j & 1) ? 2 : 3) * TILE];
-      return *reinterpret_cast<const bf16x8*>(&t[32 * db * BQ + (tbase ^ (16 * c))]);
+      const char* t = reinterpret_cast<const char*>(&stage[b][((j & 1) ? 0 : 1) * TILE]) + 16 * c * HD * 2;
+      return read_tr_pair(t + tr_off[db][0], t + tr_off[db][1]);
     }
   };
   // -D of rows 32qb + 8g4 + 4hi + 0..3 (the dP accumulators' start), from buffer b
@@ -339,7 +341,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   if (it1 - it0 > 2) next_item(h2, t2);
   if (it0 < it1) {
     uint32_t vq = 0;
-    for (int j = 0; j < 16; ++j) dma_step(j, src0, 0, vq);
+    for (int j = 0; j < 8; ++j) dma_step(j, src0, 0, vq);
     load_scalars(src0);
     wait_vmem();
     store_scalars(0);
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
               load_rows(IC<qb>{}, IC<g4>{});
             }
             if constexpr (i >= 8 && i < 12) load_nd(IC<1>{}, IC<i - 8>{}, buf);
-            if constexpr (i % 2 == 1 && i < 32) dma_step(i / 2, nx, buf ^ 1, vq);   // item it+1
+            if constexpr (i % 4 == 1 && i < 32) dma_step(i / 4, nx, buf ^ 1, vq);   // item it+1
             if constexpr (i == 2) load_scalars(nx);                               // its row scalars
             if constexpr (i == 50) nx2 = item_src(h2, t2);                      // where item it+2 is
             if constexpr (i == 56) {
@@ -567,10 +569,8 @@ int bwd_kv_split(int64_t Sq, int64_t Sk, int32_t Hkv) {
 }
 
 size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D) {
-  const size_t sq_pad = (size_t)transpose_perm16_padded_len(Sq);
   const size_t sk_pad = (size_t)transpose_perm16_padded_len(Sk);
   size_t n = align256((size_t)Sq * Hq * sizeof(float))                       // D
-             + 2 * align256((size_t)Hq * D * sq_pad * sizeof(bf16))           // q^T, dout^T
              + align256((size_t)Hkv * D * sk_pad * sizeof(bf16))              // k^T
              + align256(n_kv_blocks(Sk) * sizeof(int))                        // key-block order
              + align256(n_dq_tiles(Sq) * sizeof(int));                        // dQ tile order
@@ -582,15 +582,10 @@ size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv,
 
 void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
   const AttnArgs& f = a.f;
-  a.sq_pad = transpose_perm16_padded_len(f.Sq);
   a.sk_pad = transpose_perm16_padded_len(f.Sk);
   char* p = reinterpret_cast<char*>(base);
   a.delta = reinterpret_cast<float*>(p);
   p += align256((size_t)f.Sq * f.Hq * sizeof(float));
-  a.qt = p;
-  p += align256((size_t)f.Hq * HD * a.sq_pad * sizeof(bf16));
-  a.dot = p;
-  p += align256((size_t)f.Hq * HD * a.sq_pad * sizeof(bf16));
   a.kt = p;
   p += align256((size_t)f.Hkv * HD * a.sk_pad * sizeof(bf16));
   a.kv_order = reinterpret_cast<int*>(p);
@@ -609,10 +604,9 @@ void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
 }
 
 bool attn_bwd_supported(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv) {
-  // byte offsets inside one head of the head-dim-major copies, and inside one tile
+  // byte offsets inside one head of the head-dim-major copy of k, and inside one tile
   // of q, dout, k and v, are 32-bit
-  return (int64_t)HD * transpose_perm16_padded_len(Sq) * 2 <= (int64_t)UINT32_MAX &&
-         (int64_t)HD * transpose_perm16_padded_len(Sk) * 2 <= (int64_t)UINT32_MAX &&
+  return (int64_t)HD * transpose_perm16_padded_len(Sk) * 2 <= (int64_t)UINT32_MAX &&
          (int64_t)(BQ + 1) * Hq * HD * 2 <= (int64_t)UINT32_MAX &&
          (int64_t)(BQ + 1) * Hkv * HD * 2 <= (int64_t)UINT32_MAX;
 }
@@ -623,9 +617,6 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   if (rows > 0) {
     hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0,
                        stream, a);
-    hipError_t e = launch_transpose_perm16(f.q, f.lq, f.Sq, f.Hq, a.qt, stream);
-    if (e == hipSuccess) e = launch_transpose_perm16(a.dout, f.lq, f.Sq, f.Hq, a.dot, stream);
-    if (e != hipSuccess) return e;
   }
   if (f.Sk > 0) {
     hipError_t e = launch_transpose_perm16(f.k, f.lk, f.Sk, f.Hkv, a.kt, stream);

@@ -82,6 +82,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16) of a row-major bf16 matrix M: in each group
+// of 16 lanes, lane s names the 8 bytes M[k0 + s/4][m0 + 4(s%4) .. +3] and lane i of the
+// group receives M[k0 .. k0+3][m0 + i].  Two such reads four rows apart (in k) give one
+// MFMA A operand whose reduction slots run along M's rows.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 read_tr_pair(const char* lo, const char* hi) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(__attribute__((address_space(3))) const char*)lo);
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(__attribute__((address_space(3))) const char*)hi);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // max(x, x of the lane 32 apart), on the VALU (v_permlane32_swap: each lane ends up
 // with both values of its pair, in some order)
 __device__ __forceinline__ float max_xor32(float x) {
