@@ -7,9 +7,7 @@
 //
 // Kernels, in stream order:
 //   1. pre:       D_i for every (row, head);
-//   2. transpose: the head-dim-major copy of k in the workspace (transpose.hip) for
-//                 the dQ kernel;
-//   3. dK, dV:    a workgroup owns 128 keys of one key/value head (32 per wave; K
+//   2. dK, dV:    a workgroup owns 128 keys of one key/value head (32 per wave; K
 //                 and V of the lane's key are B operands in registers) and walks the
 //                 64-row query tiles that can see the block, for every query head of
 //                 the group (one "item" = one (head, tile) pair).  An item is Q and
@@ -26,7 +24,7 @@
 //                 the matrix core's execution hides: the next item's DMA (spread over
 //                 the whole item), and P and dS of the previous 32 rows (exp2,
 //                 products, bf16 packing);
-//   4. dQ:        attn_bwd_dq.hip, query-stationary, recomputing S and dP (no atomics).
+//   3. dQ:        attn_bwd_dq.hip, query-stationary, recomputing S and dP (no atomics).
 // Query tiles that cannot see the key block are not visited (the first visible
 // tile follows from the block's first key, the last from a binary search over
 // document starts).  Fully visible tiles run first, without any masking work; the
@@ -569,9 +567,7 @@ int bwd_kv_split(int64_t Sq, int64_t Sk, int32_t Hkv) {
 }
 
 size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D) {
-  const size_t sk_pad = (size_t)transpose_perm16_padded_len(Sk);
   size_t n = align256((size_t)Sq * Hq * sizeof(float))                       // D
-             + align256((size_t)Hkv * D * sk_pad * sizeof(bf16))              // k^T
              + align256(n_kv_blocks(Sk) * sizeof(int))                        // key-block order
              + align256(n_dq_tiles(Sq) * sizeof(int));                        // dQ tile order
   const int qs = bwd_dq_split(Sq, Sk, Hq), ks = bwd_kv_split(Sq, Sk, Hkv);
@@ -582,12 +578,9 @@ size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv,
 
 void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
   const AttnArgs& f = a.f;
-  a.sk_pad = transpose_perm16_padded_len(f.Sk);
   char* p = reinterpret_cast<char*>(base);
   a.delta = reinterpret_cast<float*>(p);
   p += align256((size_t)f.Sq * f.Hq * sizeof(float));
-  a.kt = p;
-  p += align256((size_t)f.Hkv * HD * a.sk_pad * sizeof(bf16));
   a.kv_order = reinterpret_cast<int*>(p);
   p += align256(n_kv_blocks(f.Sk) * sizeof(int));
   a.dq_order = reinterpret_cast<int*>(p);
@@ -604,10 +597,8 @@ void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
 }
 
 bool attn_bwd_supported(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv) {
-  // byte offsets inside one head of the head-dim-major copy of k, and inside one tile
-  // of q, dout, k and v, are 32-bit
-  return (int64_t)HD * transpose_perm16_padded_len(Sk) * 2 <= (int64_t)UINT32_MAX &&
-         (int64_t)(BQ + 1) * Hq * HD * 2 <= (int64_t)UINT32_MAX &&
+  // byte offsets inside one tile of q, dout, k and v are 32-bit
+  return (int64_t)(BQ + 1) * Hq * HD * 2 <= (int64_t)UINT32_MAX &&
          (int64_t)(BQ + 1) * Hkv * HD * 2 <= (int64_t)UINT32_MAX;
 }
 
@@ -619,11 +610,9 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
                        stream, a);
   }
   if (f.Sk > 0) {
-    hipError_t e = launch_transpose_perm16(f.k, f.lk, f.Sk, f.Hkv, a.kt, stream);
-    if (e != hipSuccess) return e;
     const int n_ktiles = (f.Sk + BKV - 1) / BKV;
     const int n_qtiles = (f.Sq + BQ - 1) / BQ;
-    e = launch_schedule_kv_blocks(f, n_ktiles, BKV, BQ, a.kv_order, stream);
+    hipError_t e = launch_schedule_kv_blocks(f, n_ktiles, BKV, BQ, a.kv_order, stream);
     if (e != hipSuccess) return e;
     if (a.kv_split > 1) {
       hipLaunchKernelGGL(attn_bwd_main_kernel<true>, dim3((unsigned)(n_ktiles * f.Hkv * a.kv_split)),

@@ -10,9 +10,8 @@
 //   * a workgroup is 8 wavefronts (2 per SIMD) and owns 256 query rows of one head;
 //     each wave owns 32 rows with their Q and dO fragments in registers;
 //   * key tiles of 64 keys are staged in double-buffered LDS by LDS-DMA one tile
-//     ahead: K and V row-major, and K^T from the head-dim-major copy made for the
-//     dK/dV kernel (token order inside each 16-token group = the lanes' score
-//     slots), so every MFMA operand read from LDS is one 16-byte read;
+//     ahead: K and V row-major; the K^T operand of dQ^T is read from the K tile with
+//     the transposing LDS read (two 8-byte reads per MFMA operand);
 //   * S^T = K Q^T and dP^T = V dO^T come out with one query per lane (32 MFMAs,
 //     two interleaved accumulator chains each); P and dS are formed in registers and
 //     dS^T (bf16) feeds dQ^T += K^T dS^T directly (16 MFMAs);
@@ -42,8 +41,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   constexpr int BR = 32 * NW;              // query rows per workgroup
   constexpr int NL = TILE / 8 / (NW * 64); // 64-lane DMA loads per wave per staged tile
   static_assert(NL * NW * 64 * 8 == TILE, "a staged tile is a whole number of loads per wave");
-  // per buffer: K [64 keys][128], V [64 keys][128] (swz16), K^T [128][64 positions] (swz8)
-  __shared__ __attribute__((aligned(16))) bf16 stage[2][3 * TILE];
+  // per buffer: K [64 keys][128], V [64 keys][128] (swz16)
+  __shared__ __attribute__((aligned(16))) bf16 stage[2][2 * TILE];
   __shared__ int red[NW][2];
 
   const AttnArgs& f = a.f;
@@ -113,47 +112,52 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   asm volatile("" :: "v"(lse2), "v"(dlt));
   const float sl2 = f.scale * USP_LOG2E;
 
-  // ---- staging by LDS-DMA: tile u (K, V, K^T), load i (0..NL-1) of wave w covers
-  // physical chunks [(NW i + w) * 64, +64), lane l the chunk (NW i + w) * 64 + l:
-  //   K, V: key row 4 NW i + 4w + l/16, physical chunk l%16;
-  //   K^T:  head-dim row 8 NW i + 8w + l/8, physical chunk l%8.
-  // The swizzles depend on the row modulo 16 only, so one lane offset serves all loads.
+  // ---- staging by LDS-DMA: tile u (K, V), load i (0..NL-1) of wave w covers physical
+  // chunks [(NW i + w) * 64, +64), lane l the chunk (NW i + w) * 64 + l: key row
+  // 4 NW i + 4w + l/16, physical chunk l%16.  The swizzle depends on the row modulo 16
+  // only, so one lane offset serves all loads.
   const uint32_t kr0 = (uint32_t)(4 * wave + (lane >> 4));
   const uint32_t k_lc = (uint32_t)((((lane & 15) ^ swz16(kr0)) << 3) * 2);
   const uint32_t rowkB = (uint32_t)f.lk.row_stride * 2;          // bytes per k / v row
-  const int td0 = 8 * wave + (lane >> 3);
-  const uint32_t t_off = (uint32_t)((td0 * a.sk_pad + (((lane & 7) ^ swz8(td0)) << 3)) * 2);
   const uint32_t stage_lds = lds_addr(&stage[0][0]);
   auto dma_step = [&](int s, int kt, int buf) {   // s = NL u + i
     const int u = s / NL, i = s % NL;
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
-        stage_lds + (uint32_t)(((buf * 3 + u) * TILE + (NW * i + wave) * 512) * 2));
-    if (u < 2) {   // keys past Sk are clamped to the last key (the mask zeroes them)
-      const uint32_t lim = (uint32_t)(f.Sk - 1 - kt);
-      const uint32_t voff = min(kr0 + 4 * NW * i, lim) * rowkB + k_lc;
-      const char* base = reinterpret_cast<const char*>(u == 0 ? f.k : f.v) + rows_off(f.lk, kt, hk) * 2;
-      dma16(base, voff, lds);
-    } else {
-      const char* base = reinterpret_cast<const char*>(a.kt) +
-                         (((int64_t)hk * HD + 8 * NW * i) * a.sk_pad + kt) * 2;
-      dma16(base, t_off, lds);
-    }
+        stage_lds + (uint32_t)(((buf * 2 + u) * TILE + (NW * i + wave) * 512) * 2));
+    // keys past Sk are clamped to the last key (the mask zeroes them)
+    const uint32_t lim = (uint32_t)(f.Sk - 1 - kt);
+    const uint32_t voff = min(kr0 + 4 * NW * i, lim) * rowkB + k_lc;
+    const char* base = reinterpret_cast<const char*>(u == 0 ? f.k : f.v) + rows_off(f.lk, kt, hk) * 2;
+    dma16(base, voff, lds);
   };
 
   // per-lane element offsets inside the tiles: chunk 2k + hi of row r sits at
   // (2k + hi) ^ swz(r), i.e. at  base ^ 16k  with base = r * len + 8 (hi ^ swz(r))
   //   K, V (A operands of S^T, dP^T): row 32 kb2 + r32, chunks 2 kk + hi
-  //   K^T (A operand of dQ^T): head-dim row 32 db + r32, chunks 2c + hi (positions
-  //   16c + 8hi .. +7 = the lane half's eight key slots of chunk c)
   const int kbase = r32 * HD + ((hi ^ swz16(r32)) << 3);
-  const int tbase = r32 * BC + ((hi ^ swz8(r32)) << 3);
+  //   K transposed (A operand of dQ^T: head-dim row d = r32 + 32db, reduction slots =
+  //   keys 16c + 8(s/4) + 4hi + s%4, the score accumulator's key order): in 16-lane
+  //   group g, lane s names key row 16c + 8half + 4(g/2) + s/4 at columns
+  //   32db + 16(g%2) + 4(s%4); the row's swizzle is swz16(row in the group) ^ 2half and
+  //   db flips chunk bits 2-3, so the byte offset is (tr0 ^ 64db ^ 32half) + (16c + 8half) * 256.
+  uint32_t tr_off[4][2];
+  {
+    const int g = lane >> 4, s = lane & 15;
+    const int trow = 4 * (g >> 1) + (s >> 2), tcol = 16 * (g & 1) + 4 * (s & 3);
+    const uint32_t tr0 = (uint32_t)(trow * HD * 2 + (((tcol >> 3) ^ swz16(trow)) << 4) + (tcol & 7) * 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      tr_off[db][0] = tr0 ^ (uint32_t)(64 * db);
+      tr_off[db][1] = (tr0 ^ (uint32_t)(64 * db + 32)) + 8 * HD * 2;
+    }
+  }
 
   f32x16 dqacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dqacc[i] = f32x16{};
 
   if (kb < ke) {
-    for (int s = 0; s < 3 * NL; ++s) dma_step(s, kb, 0);
+    for (int s = 0; s < 2 * NL; ++s) dma_step(s, kb, 0);
     wait_vmem();
     __syncthreads();
   }
@@ -162,7 +166,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   for (int kt = kb; kt < ke; kt += BC, buf ^= 1) {
     const bf16* Kb = &stage[buf][0];
     const bf16* Vb = &stage[buf][TILE];
-    const bf16* Tb = &stage[buf][2 * TILE];
     const int ktn = min(kt + BC, last_kt);   // the last tile fetches itself again (unused)
 
     // ---- S^T and dP^T: 64 keys x 32 queries each.  MFMA i: S (even i) or dP (odd i)
@@ -182,9 +185,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
         },
         [&](auto I) {
           constexpr int i = decltype(I)::v;
-          // the 3 NL loads spread over the 32 MFMAs
-          constexpr int every = 32 / (4 * NL);
-          if constexpr (i % every == 1 % every && i / every < 3 * NL) dma_step(i / every, ktn, buf ^ 1);
+          // the 2 NL loads spread over the 32 MFMAs
+          constexpr int every = 32 / (2 * NL);
+          if constexpr (i % every == 1 % every && i / every < 2 * NL) dma_step(i / every, ktn, buf ^ 1);
         });
 
     __builtin_amdgcn_s_setprio(0);
@@ -220,7 +223,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
     mfma_pipeline<PF, 16>(
         [&](auto I) {
           constexpr int i = decltype(I)::v, c = i >> 2, db = i & 3;
-          return *reinterpret_cast<const bf16x8*>(&Tb[32 * db * BC + (tbase ^ (16 * c))]);
+          const char* t = reinterpret_cast<const char*>(Kb) + 16 * c * HD * 2;
+          return read_tr_pair(t + tr_off[db][0], t + tr_off[db][1]);
         },
         [&](auto I, const bf16x8& op) {
           constexpr int i = decltype(I)::v, c = i >> 2, db = i & 3;

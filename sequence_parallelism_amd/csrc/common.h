@@ -167,10 +167,8 @@ struct AttnBwdArgs {
   void* dv;
   // workspace regions
   float* delta;        // [Hq][Sq] fp32
-  void* kt;            // [Hkv][D][sk_pad] bf16, head-dim-major k
   int* kv_order;       // key blocks of the dK/dV kernel, heaviest first
   int* dq_order;       // query tiles of the dQ kernel, heaviest first
-  int64_t sk_pad;
   // split key ranges of the dQ kernel (dq_split > 1): partial dQ^T sums per chunk,
   // dq_part [Hq][tiles][dq_split][256][128] fp32, summed by a combine pass
   int dq_split;
