@@ -240,9 +240,9 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(dominant),
-                "kernel": "usp_ulysses_attn_bwd call: D pre-pass, head-dim-major copies, launch-order "
-                          "schedules, dK/dV kernel, dQ kernel" if dominant == "bwd"
-                else "usp_ulysses_attn_fwd call: V^T copy, launch-order schedule, attention kernel"}
+                "kernel": "usp_ulysses_attn_bwd call: D pre-pass, launch-order schedules, dK/dV kernel, "
+                          "dQ kernel" if dominant == "bwd"
+                else "usp_ulysses_attn_fwd call: launch-order schedule, attention kernel"}
 
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)

@@ -122,8 +122,9 @@ usp_status usp_head_to_seq_permute(void* dst, const void* src, int32_t P, int64_
  * Supported: in_dtype BF16 with D = 128 (MFMA path; o_dtype BF16 or F32);
  *            in_dtype F32 with 1 <= D <= 128 (o_dtype F32).
  * workspace: caller-owned device buffer of at least blockattn_fwd_workspace_size()
- *   bytes, 16-byte aligned (the bf16 path keeps a head-dim-major copy of v and the
- *   launch order of the query tiles there; the f32 path needs none and accepts NULL).  Its contents on entry do not
+ *   bytes, 16-byte aligned (the bf16 path keeps the launch order of the query tiles
+ *   there, and the partial results of a call whose key ranges it splits; the f32 path
+ *   needs none and accepts NULL).  Its contents on entry do not
  *   matter and are clobbered; it must not overlap any other argument.
  * Alignment: bf16 q, k, v, o 16-byte aligned.
  * Errors: NULL pointers (position_ids only when causal); Sq, Sk < 0; Hq, Hkv < 1;

@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libusp.so")
-SOURCES = ["usp_abi.hip", "permute.hip", "merge.hip", "transpose.hip", "attn_fwd.hip", "attn_bwd.hip",
+SOURCES = ["usp_abi.hip", "permute.hip", "merge.hip", "attn_fwd.hip", "attn_bwd.hip",
            "attn_bwd_dq.hip", "schedule.hip"]
 
 # gfx950 only; packed-FP32 VALU instructions disabled.

@@ -10,10 +10,9 @@
 // bf16 / head dim 128 kernel (MFMA):
 //   * a workgroup is 8 wavefronts (2 per SIMD) and owns 256 query rows of one head;
 //     each wave owns 32 rows and keeps its Q fragment in registers;
-//   * key tiles of 64 keys are staged in double-buffered LDS: K row-major, and V
-//     from its head-dim-major copy (V^T, made once per call by transpose.hip), so
-//     every MFMA operand taken from LDS is ONE 16-byte read (LDS instruction issue,
-//     not bytes, is what limits narrower reads on gfx950).  The next tile comes by
+//   * key tiles of 64 keys are staged in double-buffered LDS, K and V row-major; the
+//     S^T operands are 16-byte reads of K, the O^T operands (V transposed) two
+//     8-byte transposing reads of V (ds_read_b64_tr_b16).  The next tile comes by
 //     LDS-DMA, issued behind the current tile's score MFMAs, so one barrier per
 //     tile suffices and memory latency is hidden behind the MFMA work; operand
 //     reads run four MFMAs ahead of their use;
@@ -59,7 +58,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   constexpr int BR = 32 * NW;              // query rows per workgroup
   constexpr int NL = TILE / 8 / (NW * 64); // 64-lane DMA loads per wave per staged tile
   static_assert(NL * NW * 64 * 8 == TILE, "a staged tile is a whole number of loads per wave");
-  // per buffer: K [64 keys][128] (swz16), V^T [128][64 positions] (swz8)
+  // per buffer: K [64 keys][128], V [64 keys][128] (swz16)
   __shared__ __attribute__((aligned(16))) bf16 stage[2][2 * TILE];
   __shared__ int red[NW][2];
 
@@ -120,29 +119,22 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
     for (int kk = 0; kk < 8; ++kk) asm volatile("" :: "v"(qf[kk]));
   }
 
-  // ---- staging by LDS-DMA: tile u (K, V^T), load i (0..NL-1) of wave w covers
-  // physical chunks [(NW i + w) * 64, +64), lane l the chunk (NW i + w) * 64 + l:
-  //   K:   key row 4 NW i + 4w + l/16, physical chunk l%16;
-  //   V^T: head-dim row 8 NW i + 8w + l/8, physical chunk l%8.
-  // The swizzles depend on the row modulo 16 only, so one lane offset serves all loads.
+  // ---- staging by LDS-DMA: tile u (K, V), load i (0..NL-1) of wave w covers physical
+  // chunks [(NW i + w) * 64, +64), lane l the chunk (NW i + w) * 64 + l: key row
+  // 4 NW i + 4w + l/16, physical chunk l%16.  The swizzle depends on the row modulo 16
+  // only, so one lane offset serves all loads.
   const uint32_t kr0 = (uint32_t)(4 * wave + (lane >> 4));
   const uint32_t k_lc = (uint32_t)((((lane & 15) ^ swz16(kr0)) << 3) * 2);
   const uint32_t rowkB = (uint32_t)a.lk.row_stride * 2;          // bytes per k row
-  const int td0 = 8 * wave + (lane >> 3);
-  const uint32_t t_off = (uint32_t)((td0 * a.vt_ld + (((lane & 7) ^ swz8(td0)) << 3)) * 2);
   const uint32_t stage_lds = lds_addr(&stage[0][0]);
   auto dma_step = [&](int s, int kt, int buf) {   // s = NL u + i
     const int u = s / NL, i = s % NL;
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         stage_lds + (uint32_t)(((buf * 2 + u) * TILE + (NW * i + wave) * 512) * 2));
-    if (u == 0) {   // keys past Sk are clamped to the last key (the mask zeroes them)
-      const uint32_t lim = (uint32_t)(a.Sk - 1 - kt);
-      const uint32_t voff = min(kr0 + 4 * NW * i, lim) * rowkB + k_lc;
-      dma16(reinterpret_cast<const char*>(a.k) + rows_off(a.lk, kt, hk) * 2, voff, lds);
-    } else {        // the padded copy covers every position of the tile
-      dma16(reinterpret_cast<const char*>(a.vt) + (((int64_t)hk * HD + 8 * NW * i) * a.vt_ld + kt) * 2,
-            t_off, lds);
-    }
+    // keys past Sk are clamped to the last key (the mask zeroes them; P is 0 there)
+    const uint32_t lim = (uint32_t)(a.Sk - 1 - kt);
+    const uint32_t voff = min(kr0 + 4 * NW * i, lim) * rowkB + k_lc;
+    dma16(reinterpret_cast<const char*>(u == 0 ? a.k : a.v) + rows_off(a.lk, kt, hk) * 2, voff, lds);
   };
 
   const float sl2 = a.scale * USP_LOG2E;
@@ -155,10 +147,23 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   // per-lane element offsets inside the tiles: chunk 2k + hi of row r sits at
   // (2k + hi) ^ swz(r), i.e. at  base ^ 16k  with base = r * len + 8 (hi ^ swz(r))
   //   K (A operand of S^T): row 32 kb2 + r32, chunks 2 kk + hi
-  //   V^T (A operand of O^T): row 32 db + r32, chunks 2c + hi (positions 16c + 8hi ..
-  //   +7 = the lane half's eight key slots of chunk c)
   const int kbase = r32 * HD + ((hi ^ swz16(r32)) << 3);
-  const int vbase = r32 * BC + ((hi ^ swz8(r32)) << 3);
+  //   V transposed (A operand of O^T: head-dim row d = r32 + 32db, reduction slots =
+  //   keys 16c + 8(s/4) + 4hi + s%4, the score accumulator's key order): in 16-lane
+  //   group g, lane s names key row 16c + 8half + 4(g/2) + s/4 at columns
+  //   32db + 16(g%2) + 4(s%4); the row's swizzle is swz16(row in the group) ^ 2half and
+  //   db flips chunk bits 2-3, so the byte offset is (tr0 ^ 64db ^ 32half) + (16c + 8half) * 256.
+  uint32_t tr_off[4][2];
+  {
+    const int g = lane >> 4, s = lane & 15;
+    const int trow = 4 * (g >> 1) + (s >> 2), tcol = 16 * (g & 1) + 4 * (s & 3);
+    const uint32_t tr0 = (uint32_t)(trow * HD * 2 + (((tcol >> 3) ^ swz16(trow)) << 4) + (tcol & 7) * 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      tr_off[db][0] = tr0 ^ (uint32_t)(64 * db);
+      tr_off[db][1] = (tr0 ^ (uint32_t)(64 * db + 32)) + 8 * HD * 2;
+    }
+  }
 
   if (kb < ke) {
     for (int s = 0; s < 2 * NL; ++s) dma_step(s, kb, 0);
@@ -242,7 +247,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
     mfma_pipeline<PF, 16>(
         [&](auto I) {
           constexpr int i = decltype(I)::v;
-          return *reinterpret_cast<const bf16x8*>(&Vb[32 * (i & 3) * BC + (vbase ^ (16 * (i >> 2)))]);
+          const char* t = reinterpret_cast<const char*>(Vb) + 16 * (i >> 2) * HD * 2;
+          return read_tr_pair(t + tr_off[i & 3][0], t + tr_off[i & 3][1]);
         },
         [&](auto I, const bf16x8& op) {
           constexpr int i = decltype(I)::v;
@@ -383,14 +389,13 @@ int fwd_ksplit(int64_t Sq, int64_t Sk, int32_t Hq) {
   return (int)std::min<int64_t>(16, (4 * (int64_t)cus + wg - 1) / wg);
 }
 
-// workspace: V^T copy [Hkv][D][padded Sk] bf16, the query-tile order (sized for the
-// 128-row tiles of the 4-wave variant), and with a key-range split the partials
+// workspace: the query-tile order (sized for the 128-row tiles of the 4-wave
+// variant), and with a key-range split the partials
 // o_part [Hq][tiles][ksplit][256][128] and lse_part [Hq][tiles][ksplit][256] (fp32)
 size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D, int bf16_path) {
   if (!bf16_path) return 0;
   const size_t n_qtiles = (size_t)((Sq + 127) / 128);
-  size_t n = align256((size_t)Hkv * D * transpose_perm16_padded_len(Sk) * sizeof(bf16)) +
-             align256(n_qtiles * sizeof(int));
+  size_t n = align256(n_qtiles * sizeof(int));
   const int ks = fwd_ksplit(Sq, Sk, Hq);
   if (ks > 1) {
     const size_t slots = (size_t)Hq * (size_t)((Sq + 255) / 256) * ks;
@@ -401,9 +406,6 @@ size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv,
 
 void attn_fwd_workspace_layout(AttnArgs& a, void* base) {
   char* p = reinterpret_cast<char*>(base);
-  a.vt = p;
-  a.vt_ld = transpose_perm16_padded_len(a.Sk);
-  p += align256((size_t)a.Hkv * a.D * a.vt_ld * sizeof(bf16));
   a.q_order = reinterpret_cast<int*>(p);
   p += align256((size_t)((a.Sq + 127) / 128) * sizeof(int));
   a.ksplit = fwd_ksplit(a.Sq, a.Sk, a.Hq);
@@ -453,14 +455,10 @@ int device_cu_count() {
   return n;
 }
 
-// a.vt must point at a workspace of attn_fwd_workspace_bytes (laid out by
-// attn_fwd_workspace_layout); V^T is filled here.
+// a.q_order (and the partials of a split call) must point into a workspace of
+// attn_fwd_workspace_bytes laid out by attn_fwd_workspace_layout.
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t stream) {
   if (a.Sq == 0) return hipSuccess;
-  if (a.Sk > 0) {
-    hipError_t e = launch_transpose_perm16(a.v, a.lk, a.Sk, a.Hkv, const_cast<void*>(a.vt), stream);
-    if (e != hipSuccess) return e;
-  }
   if (a.ksplit > 1) return launch_fwd_nw<8, true>(a, o_f32, stream);
   const int64_t wg256 = (int64_t)((a.Sq + 255) / 256) * a.Hq;
   if (wg256 < device_cu_count()) return launch_fwd_nw<4, false>(a, o_f32, stream);

@@ -91,8 +91,6 @@ struct AttnArgs {
   int32_t q_stride, k_stride;
   int32_t causal;
   float scale;
-  const void* vt;      // bf16 path: V in head-dim-major layout (see transpose.hip)
-  int64_t vt_ld;       // its padded token length
   int* q_order;        // bf16 path: query tiles heaviest first (schedule.hip)
   // bf16 forward with split key ranges (ksplit > 1): each query tile's visible keys
   // are cut into ksplit chunks, one workgroup each, whose normalised partial O and
@@ -155,7 +153,7 @@ __device__ __forceinline__ int first_row_seeing(const AttnArgs& a, int j) {
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t s);
 int device_cu_count();
 size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D, int bf16_path);
-// fills a.vt, a.vt_ld and a.q_order from the workspace base (bf16 path)
+// fills a.q_order (and the split partials) from the workspace base (bf16 path)
 void attn_fwd_workspace_layout(AttnArgs& a, void* base);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t s);
 
@@ -197,11 +195,6 @@ hipError_t launch_schedule_kv_blocks(const AttnArgs& a, int n_blocks, int bkv, i
                                      hipStream_t s);
 hipError_t launch_schedule_q_tiles(const AttnArgs& a, int n_tiles, int br, int* order, hipStream_t s);
 
-// Y[h][d][p] = X[tok(p)][h][d] over a padded token axis, 16-token groups permuted
-// to MFMA slot order (transpose.hip); D = 128, bf16.
-int64_t transpose_perm16_padded_len(int64_t S);
-hipError_t launch_transpose_perm16(const void* x, const RowLayout& lx, int64_t S, int32_t H, void* y,
-                                   hipStream_t s);
 
 struct MergeArgs {
   void* o_acc;

@@ -14,13 +14,10 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// LDS tiles are unpadded; 16-byte chunk c of row r is stored at c ^ swz(r).  With
-// these, 16 lanes reading 16 consecutive rows at one logical chunk touch all 64
-// banks once.  Rows of 128 bf16 have 16 chunks, rows of 64 bf16 have 8, rows of 32
-// bf16 have 4.
+// LDS tiles (rows of 128 bf16 = 16 chunks of 16 bytes) are unpadded; chunk c of row r
+// is stored at c ^ swz16(r).  With it, 16 lanes reading 16 consecutive rows at one
+// logical chunk touch all 64 banks once.
 __device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
 
 // Compile-time loop: f(IC<0>{}), f(IC<1>{}), ..., so every index is a constant.
 template <int N> struct IC { static constexpr int v = N; };

@@ -64,8 +64,6 @@ AttnArgs make_args(const void* q, const void* k, const void* v, int64_t Sq, int6
   a.q_stride = 1; a.k_stride = 1;
   a.causal = causal ? 1 : 0;
   a.scale = scale;
-  a.vt = nullptr;
-  a.vt_ld = 0;
   a.q_order = nullptr;
   a.ksplit = 1;
   a.o_part = nullptr;

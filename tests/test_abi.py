@@ -104,7 +104,7 @@ def test_fwd_validation(lib):
 def test_bwd_validation(lib):
     n = ctypes.c_size_t(0)
     assert lib.blockattn_bwd_workspace_size(256, 256, 4, 1, 128, ctypes.byref(n)) == OK
-    assert n.value >= 256 * 4 * 128 * 4 + 256 * 4 * 4
+    assert n.value >= 256 * 4 * 4                       # at least D, fp32 per (row, head)
     assert lib.blockattn_bwd_workspace_size(256, 256, 4, 1, 128, None) == NULLP
     assert lib.blockattn_bwd_workspace_size(-1, 256, 4, 1, 128, ctypes.byref(n)) == SHAPE
 
