@@ -66,15 +66,30 @@ __device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const b
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-// ---- 1. D = rowsum(dO * O) -------------------------------------------------------------
+// ---- 1. D = rowsum(dO * O), and the row scalars of the dK/dV kernel -----------------
+// For every (row, head) with row < rs_ld (Sq rounded up to the 64-row tile): D, and in
+// the planes of a.rs lse log2(e), -D, and (head 0) the row's visible keys [klo, khi)
+// (row_keys); rows past Sq get 0, 0 and the empty range [KBIG, -KBIG).
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t rid = gid >> 4;        // (row, head) pair, 16 lanes each
   const int sub = threadIdx.x & 15;
   const AttnArgs& f = a.f;
-  if (rid >= (int64_t)f.Sq * f.Hq) return;
+  if (rid >= (int64_t)a.rs_ld * f.Hq) return;
   const int row = (int)(rid / f.Hq);
   const int h = (int)(rid - (int64_t)row * f.Hq);
+  const int64_t ld = a.rs_ld;
+  float* lse2p = reinterpret_cast<float*>(a.rs) + (int64_t)h * ld + row;
+  float* ndp = reinterpret_cast<float*>(a.rs) + ((int64_t)f.Hq + h) * ld + row;
+  int* klop = reinterpret_cast<int*>(a.rs) + 2 * (int64_t)f.Hq * ld + row;
+  int* khip = klop + ld;
+  if (row >= f.Sq) {   // padding rows: no work, an empty key range
+    if (sub == 0) *lse2p = 0.f;
+    if (sub == 1) *ndp = 0.f;
+    if (h == 0 && sub == 2) *klop = KBIG;
+    if (h == 0 && sub == 3) *khip = -KBIG;
+    return;
+  }
   const int64_t off = rows_off(f.lq, row, h) + sub * 8;
   const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(f.o) + off);
   const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.dout) + off);
@@ -83,7 +98,17 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
   for (int j = 0; j < 8; ++j) acc += (float)o8[j] * (float)d8[j];
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (sub == 0) a.delta[(int64_t)h * f.Sq + row] = acc;
+  if (sub == 0) {
+    a.delta[(int64_t)h * f.Sq + row] = acc;
+    *lse2p = f.lse[(int64_t)h * f.lse_ld + row] * USP_LOG2E;
+  }
+  if (sub == 1) *ndp = -acc;
+  if (h == 0 && sub == 2) {
+    int lo, hiex;
+    row_keys(f, row, lo, hiex);
+    *klop = lo;
+    *khip = hiex;
+  }
 }
 
 // ---- 3. main ----------------------------------------------------------------------
@@ -93,10 +118,9 @@ template <bool SPLIT>
 __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, int n_qtiles) {
   // per buffer: Q [64 rows][128], dO [64][128] (swz16) -- 2 tiles of 16 KB
   __shared__ __attribute__((aligned(16))) bf16 stage[2][2 * TILE];
-  __shared__ __attribute__((aligned(16))) float lse2_s[2][BQ];
-  __shared__ __attribute__((aligned(16))) float ndelta_s[2][BQ];   // -D
-  __shared__ __attribute__((aligned(16))) int klo_s[2][BQ];   // visible keys [klo, khi)
-  __shared__ __attribute__((aligned(16))) int khi_s[2][BQ];
+  // per buffer, the staged item's row scalars: lse log2(e), -D, and the visible keys
+  // [klo, khi) (int32 bits), one row per element
+  __shared__ __attribute__((aligned(16))) uint32_t scal_s[4][2][BQ];
 
   const AttnArgs& f = a.f;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -217,12 +241,12 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   struct ItemSrc {
     const char* tile[2];   // Q, dO rows q0..
     uint32_t lim;          // rows past Sq are clamped to the last row (the mask zeroes them)
-    int q0;
-    const float* lse;
-    const float* delta;
-    const int* pos;
+    const uint32_t* sc;    // this wave's row-scalar plane at row q0
   };
-  const int* const pos_or_dummy = f.causal ? f.pos : reinterpret_cast<const int*>(f.lse);
+  // wave w stages row-scalar plane w of the item: lse log2(e) and -D of its head,
+  // klo and khi of its rows
+  const uint32_t* const sc_wave = a.rs + (int64_t)(wave < 2 ? wave * f.Hq : 2 * f.Hq + wave - 2) * a.rs_ld;
+  const int64_t sc_hstep = wave < 2 ? a.rs_ld : 0;
   auto item_src = [&](int h, int t) {
     ItemSrc r;
     const int q0 = t * BQ;
@@ -230,11 +254,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
     r.tile[0] = reinterpret_cast<const char*>(f.q) + rq;
     r.tile[1] = reinterpret_cast<const char*>(a.dout) + rq;
     r.lim = (uint32_t)(f.Sq - 1 - q0);
-    r.q0 = q0;
-    const int row = min(q0 + lane, f.Sq - 1);
-    r.lse = f.lse + (int64_t)h * f.lse_ld + row;
-    r.delta = a.delta + (int64_t)h * f.Sq + row;
-    r.pos = pos_or_dummy + (f.causal ? f.q_start + f.q_stride * row : 0);
+    r.sc = sc_wave + h * sc_hstep + q0;
     return r;
   };
 
@@ -247,48 +267,38 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
     dma16(src.tile[u], vq, __builtin_amdgcn_readfirstlane(lds));
   };
 
-  // Row scalars of an item, one row per lane, read one item ahead.  The reads are
-  // issued by every wave with no arithmetic on their results (that would stall the
-  // pipeline they sit in for a whole memory latency); each wave finishes one of the
-  // four and stores it at the item's publishing barrier.
-  float p_lse = 0.f, p_delta = 0.f;
-  int p_pos = 0, p_q0 = 0;
-  auto load_scalars = [&](const ItemSrc& src) {
-    p_lse = *src.lse;
-    p_delta = *src.delta;
-    p_pos = *src.pos;
-    p_q0 = src.q0;
-  };
+  // Row scalars of an item (made by the pre kernel), one row per lane, read one item
+  // ahead: wave w loads plane w, with no arithmetic on the value (that would stall the
+  // pipeline it sits in for a whole memory latency), and stores it at the item's
+  // publishing barrier.
+  uint32_t p_sc = 0;
+  auto load_scalars = [&](const ItemSrc& src) { p_sc = src.sc[lane]; };
   auto store_scalars = [&](int buf) {
-    // every wave consumes its loads here, so that none is left in flight on any path
-    // (the compiler would otherwise wait for all memory traffic before reusing them)
-    asm volatile("" :: "v"(p_lse), "v"(p_delta), "v"(p_pos));
-    const int r = p_q0 + lane;
-    const bool ok = r < f.Sq;
-    const float l2 = ok ? p_lse * USP_LOG2E : 0.f;
-    const float dl = ok ? -p_delta : 0.f;   // -D: the initial dP accumulator
-    int klo = 0, khi = f.Sk;                // the row's visible keys [klo, khi)
-    if (f.causal) row_keys_g(f, f.q_start + f.q_stride * r, p_pos, klo, khi);
-    if (!ok) { klo = KBIG; khi = -KBIG; }
-    if (wave == 0) lse2_s[buf][lane] = l2;
-    if (wave == 1) ndelta_s[buf][lane] = dl;
-    if (wave == 2) klo_s[buf][lane] = klo;
-    if (wave == 3) khi_s[buf][lane] = khi;
+    // consumed here, so that no load is left in flight on any path (the compiler
+    // would otherwise wait for all memory traffic before reusing the register)
+    asm volatile("" :: "v"(p_sc));
+    scal_s[wave][buf][lane] = p_sc;
   };
 
   // items run over all heads' fully visible tiles, then over all heads' other tiles;
   // (h, t) of items it, it+1, it+2 (the last two clamped to the last item) advance by
-  // one item per iteration
+  // one item per iteration.  Written with selects only: uniform branches here would
+  // cost more than the arithmetic.
   auto next_item = [&](int& h, int& t) {
-    if (t >= f0 && t < f1) {
-      if (++t == f1) {
-        t = f0;
-        if (++h == (hk + 1) * grp) { h = hk * grp; t = first_masked; }
-      }
-    } else {
-      if (++t == m1) t = m2;
-      if (t >= t1) { ++h; t = first_masked; }
-    }
+    const int tn = t + 1;
+    // among the fully visible tiles: wrap to the next head, after the last head to
+    // the first boundary tile of the first head
+    const bool fwrap = tn == f1;
+    const int hf = fwrap ? h + 1 : h;
+    const bool fdone = fwrap && hf == (hk + 1) * grp;
+    const int tf = fdone ? first_masked : (fwrap ? f0 : tn);
+    const int hf2 = fdone ? hk * grp : hf;
+    // among the boundary tiles [t0, m1) and [m2, t1): skip the gap, then the next head
+    const int tm0 = tn == m1 ? m2 : tn;
+    const bool mwrap = tm0 >= t1;
+    const bool in_full = t >= f0 && t < f1;
+    h = in_full ? hf2 : (mwrap ? h + 1 : h);
+    t = in_full ? tf : (mwrap ? first_masked : tm0);
   };
   f32x16 dka[4], dva[4];
 #pragma unroll
@@ -311,7 +321,7 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   f32x4 e4[2][4];
   auto load_nd = [&](auto QB, auto G4, int b) {
     constexpr int qb = decltype(QB)::v, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
-    e4[qb][g4] = *reinterpret_cast<const f32x4*>(&ndelta_s[b][q + 4 * hi]);
+    e4[qb][g4] = *reinterpret_cast<const f32x4*>(&scal_s[1][b][q + 4 * hi]);
   };
   bf16x8 ops[PF];   // operand reads in flight, carried from item to item
 
@@ -353,7 +363,6 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   auto run_item = [&](auto mask_tag, int it) {
     constexpr bool MASK = decltype(mask_tag)::v != 0;
     const int buf = (it - it0) & 1;
-    ItemSrc nx2;
     // every wave is done with item it-1, which read buffer buf ^ 1: it can be refilled
     // (item it itself was published halfway through item it-1's last slot)
     __syncthreads();
@@ -387,10 +396,10 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
       // row scalars of rows 32qb + 8g4 + 4hi + 0..3, read four steps before first use
       auto load_rows = [&](auto QB, auto G4) {
         constexpr int qb = decltype(QB)::v, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
-        l4[qb][g4] = *reinterpret_cast<const f32x4*>(&lse2_s[buf][q + 4 * hi]);
+        l4[qb][g4] = *reinterpret_cast<const f32x4*>(&scal_s[0][buf][q + 4 * hi]);
         if constexpr (MASK) {
-          const int4 lov = *reinterpret_cast<const int4*>(&klo_s[buf][q + 4 * hi]);
-          const int4 hiv = *reinterpret_cast<const int4*>(&khi_s[buf][q + 4 * hi]);
+          const int4 lov = *reinterpret_cast<const int4*>(&scal_s[2][buf][q + 4 * hi]);
+          const int4 hiv = *reinterpret_cast<const int4*>(&scal_s[3][buf][q + 4 * hi]);
           const int loa[4] = {lov.x, lov.y, lov.z, lov.w};
           const int hia[4] = {hiv.x, hiv.y, hiv.z, hiv.w};
 #pragma unroll
@@ -442,7 +451,19 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
             if constexpr (i >= 8 && i < 12) load_nd(IC<1>{}, IC<i - 8>{}, buf);
             if constexpr (i % 4 == 1 && i < 32) dma_step(i / 4, nx, buf ^ 1, vq);   // item it+1
             if constexpr (i == 2) load_scalars(nx);                               // its row scalars
-            if constexpr (i == 50) nx2 = item_src(h2, t2);                      // where item it+2 is
+            if constexpr (i == 50) {
+              // where item it+2 is (item it's last use of nx, its DMA, is behind it), and
+              // the step to item it+3; pinned here so that the compiler does not sink this
+              // scalar work to the end of the item, where no MFMA runs beside it
+              nx = item_src(h2, t2);
+              asm volatile("" :: "s"(nx.tile[0]), "s"(nx.tile[1]), "s"(nx.sc), "s"(nx.lim));
+              int hn = h2, tn = t2;
+              next_item(hn, tn);
+              const bool adv = it + 3 < it1;
+              h2 = adv ? hn : h2;
+              t2 = adv ? tn : t2;
+              asm volatile("" :: "s"(h2), "s"(t2));
+            }
             if constexpr (i == 56) {
               // item it+1 has landed (its DMA was issued in the first half of this item),
               // and so have its row scalars, which go to the other buffer; the barrier
@@ -467,8 +488,6 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
           });
     }
 
-    nx = nx2;
-    if (it + 3 < it1) next_item(h2, t2);
   };
 #pragma unroll 1
   for (int it = it0; it < min(it1, n_full); ++it) run_item(IC<0>{}, it);
@@ -567,7 +586,9 @@ int bwd_kv_split(int64_t Sq, int64_t Sk, int32_t Hkv) {
 }
 
 size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D) {
+  const size_t rs_ld = (size_t)((Sq + BQ - 1) / BQ) * BQ;
   size_t n = align256((size_t)Sq * Hq * sizeof(float))                       // D
+             + align256((2 * (size_t)Hq + 2) * rs_ld * sizeof(uint32_t))      // row scalars
              + align256(n_kv_blocks(Sk) * sizeof(int))                        // key-block order
              + align256(n_dq_tiles(Sq) * sizeof(int));                        // dQ tile order
   const int qs = bwd_dq_split(Sq, Sk, Hq), ks = bwd_kv_split(Sq, Sk, Hkv);
@@ -581,6 +602,9 @@ void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
   char* p = reinterpret_cast<char*>(base);
   a.delta = reinterpret_cast<float*>(p);
   p += align256((size_t)f.Sq * f.Hq * sizeof(float));
+  a.rs_ld = ((f.Sq + BQ - 1) / BQ) * BQ;
+  a.rs = reinterpret_cast<uint32_t*>(p);
+  p += align256((2 * (size_t)f.Hq + 2) * (size_t)a.rs_ld * sizeof(uint32_t));
   a.kv_order = reinterpret_cast<int*>(p);
   p += align256(n_kv_blocks(f.Sk) * sizeof(int));
   a.dq_order = reinterpret_cast<int*>(p);
@@ -604,7 +628,7 @@ bool attn_bwd_supported(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv) {
 
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   const AttnArgs& f = a.f;
-  const int64_t rows = (int64_t)f.Sq * f.Hq;
+  const int64_t rows = (int64_t)a.rs_ld * f.Hq;
   if (rows > 0) {
     hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0,
                        stream, a);

@@ -130,20 +130,6 @@ __device__ __forceinline__ void row_keys(const AttnArgs& a, int row, int& lo, in
   hiex = min(hiex, a.Sk);
 }
 
-// The same from the row's global index and its position_ids value (pos of gq).
-__device__ __forceinline__ void row_keys_g(const AttnArgs& a, int gq, int posv, int& lo, int& hiex) {
-  const int ds = gq - posv;
-  if (a.k_stride == 1) {
-    lo = ds - a.k_start;
-    hiex = gq - a.k_start + 1;
-  } else {
-    lo = ceil_div(ds - a.k_start, a.k_stride);
-    hiex = floor_div(gq - a.k_start, a.k_stride) + 1;
-  }
-  lo = max(lo, 0);
-  hiex = min(hiex, a.Sk);
-}
-
 // First local query row that sees local key j or a later one (causal): the smallest
 // row with q_start + q_stride row >= k_start + k_stride j, clipped at 0.
 __device__ __forceinline__ int first_row_seeing(const AttnArgs& a, int j) {
@@ -165,6 +151,10 @@ struct AttnBwdArgs {
   void* dv;
   // workspace regions
   float* delta;        // [Hq][Sq] fp32
+  // row scalars of the dK/dV kernel, planes of rs_ld (Sq rounded up to 64) rows:
+  // [Hq] lse log2(e), [Hq] -D (fp32 bits), then klo, khi (int32, the visible keys)
+  uint32_t* rs;
+  int32_t rs_ld;
   int* kv_order;       // key blocks of the dK/dV kernel, heaviest first
   int* dq_order;       // query tiles of the dQ kernel, heaviest first
   // split key ranges of the dQ kernel (dq_split > 1): partial dQ^T sums per chunk,
