@@ -215,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
 #pragma unroll
       for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[kb2][i]);
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * sl2;
+    mloc = max_xor32(mloc) * sl2;   // the row's other 32 keys sit in the lane 32 apart
     // move the max only when it grows by more than 2^RESCALE_TH
     const bool grow = mloc > m_run + RESCALE_TH;
     if (__ballot(grow)) {
