@@ -72,6 +72,7 @@ __device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const b
 // (row_keys); rows past Sq get 0, 0 and the empty range [KBIG, -KBIG).
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid == 0) *a.kv_next = 0;   // the dK/dV kernel's work queue, which runs after this kernel
   const int64_t rid = gid >> 4;        // (row, head) pair, 16 lanes each
   const int sub = threadIdx.x & 15;
   const AttnArgs& f = a.f;
@@ -112,27 +113,24 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
 }
 
 // ---- 3. main ----------------------------------------------------------------------
-// SPLIT: the workgroup takes chunk c of its key block's items (a.kv_split chunks) and
-// writes its partial dK^T, dV^T sums for the combine pass.
+// One work unit: key block kv_order[unit / (Hkv nch)] of key/value head unit % Hkv
+// (units run heaviest first, schedule.hip; the heads of one block are adjacent, then
+// the chunks of a split block).  SPLIT: the unit is chunk c of its key block's items
+// (a.kv_split chunks) and writes its partial dK^T, dV^T sums for the combine pass.
+typedef bf16 StageBuf[2][2 * 64 * 128];   // per buffer: Q [64 rows][128], dO [64][128] (swz16)
+typedef uint32_t ScalBuf[4][2][64];       // per buffer: lse log2(e), -D, klo, khi per row
 template <bool SPLIT>
-__global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, int n_qtiles) {
-  // per buffer: Q [64 rows][128], dO [64][128] (swz16) -- 2 tiles of 16 KB
-  __shared__ __attribute__((aligned(16))) bf16 stage[2][2 * TILE];
-  // per buffer, the staged item's row scalars: lse log2(e), -D, and the visible keys
-  // [klo, khi) (int32 bits), one row per element
-  __shared__ __attribute__((aligned(16))) uint32_t scal_s[4][2][BQ];
-
+__device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles, int unit, StageBuf& stage,
+                                              ScalBuf& scal_s) {
   const AttnArgs& f = a.f;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, hi = lane >> 5;
-  // key blocks start heaviest first (schedule.hip); heads of one block are adjacent,
-  // then the chunks of a split block
-  const int hk = blockIdx.x % f.Hkv;
+  const int hk = unit % f.Hkv;
   const int nch = SPLIT ? a.kv_split : 1;
-  const int chunk = SPLIT ? (blockIdx.x / f.Hkv) % nch : 0;
+  const int chunk = SPLIT ? (unit / f.Hkv) % nch : 0;
   const int n_kb = (f.Sk + BKV - 1) / BKV;              // the order is a permutation of [0, n_kb)
-  const int kbi = min(max(a.kv_order[blockIdx.x / f.Hkv / nch], 0), n_kb - 1);
+  const int kbi = min(max(a.kv_order[unit / f.Hkv / nch], 0), n_kb - 1);
   const int k0 = kbi * BKV;                             // first key
   const int kw0 = k0 + wave * 32;                       // this wave's first key
   const int kl = kw0 + r32;                             // this lane's key (B-operand column)
@@ -535,6 +533,26 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   }
 }
 
+// A persistent workgroup per CU takes units from a queue (a.kv_next, zeroed by the pre
+// kernel) in heaviest-first order until none is left.  The hardware would hand the
+// workgroups of a grid to the eight XCDs round-robin, a split fixed at launch; XCDs run
+// at measurably different speeds, and with the queue a slower one simply takes fewer
+// units.
+template <bool SPLIT>
+__global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, int n_qtiles, int n_units) {
+  __shared__ __attribute__((aligned(16))) StageBuf stage;
+  __shared__ __attribute__((aligned(16))) ScalBuf scal_s;
+  __shared__ int unit_s;
+  for (;;) {
+    __syncthreads();   // the previous unit is done with the LDS (and with unit_s)
+    if (threadIdx.x == 0) unit_s = atomicAdd(a.kv_next, 1);
+    __syncthreads();
+    const int unit = __builtin_amdgcn_readfirstlane(unit_s);
+    if (unit >= n_units) break;   // every wave sees the same unit: all leave together
+    attn_bwd_unit<SPLIT>(a, n_qtiles, unit, stage, scal_s);
+  }
+}
+
 // dK = scale * (sum of the chunk partials), dV = sum, bf16; 16 lanes per (head, key)
 __global__ __launch_bounds__(256) void attn_bwd_kv_combine_kernel(AttnBwdArgs a) {
   const AttnArgs& f = a.f;
@@ -590,6 +608,7 @@ size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv,
   size_t n = align256((size_t)Sq * Hq * sizeof(float))                       // D
              + align256((2 * (size_t)Hq + 2) * rs_ld * sizeof(uint32_t))      // row scalars
              + align256(n_kv_blocks(Sk) * sizeof(int))                        // key-block order
+             + align256(sizeof(int))                                          // dK/dV work queue
              + align256(n_dq_tiles(Sq) * sizeof(int));                        // dQ tile order
   const int qs = bwd_dq_split(Sq, Sk, Hq), ks = bwd_kv_split(Sq, Sk, Hkv);
   if (qs > 1) n += align256((size_t)Hq * (size_t)((Sq + 255) / 256) * qs * 256 * HD * sizeof(float));
@@ -607,6 +626,8 @@ void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
   p += align256((2 * (size_t)f.Hq + 2) * (size_t)a.rs_ld * sizeof(uint32_t));
   a.kv_order = reinterpret_cast<int*>(p);
   p += align256(n_kv_blocks(f.Sk) * sizeof(int));
+  a.kv_next = reinterpret_cast<int*>(p);
+  p += align256(sizeof(int));
   a.dq_order = reinterpret_cast<int*>(p);
   p += align256(n_dq_tiles(f.Sq) * sizeof(int));
   a.dq_split = bwd_dq_split(f.Sq, f.Sk, f.Hq);
@@ -628,27 +649,29 @@ bool attn_bwd_supported(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv) {
 
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   const AttnArgs& f = a.f;
+  // at least one workgroup: the pre kernel also resets the dK/dV kernel's queue
   const int64_t rows = (int64_t)a.rs_ld * f.Hq;
-  if (rows > 0) {
-    hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0,
-                       stream, a);
-  }
+  hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)std::max<int64_t>(1, (rows * 16 + 255) / 256)), dim3(256), 0,
+                     stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (f.Sk > 0) {
     const int n_ktiles = (f.Sk + BKV - 1) / BKV;
     const int n_qtiles = (f.Sq + BQ - 1) / BQ;
-    hipError_t e = launch_schedule_kv_blocks(f, n_ktiles, BKV, BQ, a.kv_order, stream);
+    e = launch_schedule_kv_blocks(f, n_ktiles, BKV, BQ, a.kv_order, stream);
     if (e != hipSuccess) return e;
+    // one persistent workgroup per CU (the kernel's registers allow one per CU)
+    const int n_units = n_ktiles * f.Hkv * a.kv_split;
+    const dim3 grid((unsigned)std::min(n_units, device_cu_count()));
     if (a.kv_split > 1) {
-      hipLaunchKernelGGL(attn_bwd_main_kernel<true>, dim3((unsigned)(n_ktiles * f.Hkv * a.kv_split)),
-                         dim3(NWB * 64), 0, stream, a, n_qtiles);
+      hipLaunchKernelGGL(attn_bwd_main_kernel<true>, grid, dim3(NWB * 64), 0, stream, a, n_qtiles, n_units);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       const int64_t threads = (int64_t)f.Hkv * f.Sk * 16;
       hipLaunchKernelGGL(attn_bwd_kv_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                          stream, a);
     } else {
-      hipLaunchKernelGGL(attn_bwd_main_kernel<false>, dim3((unsigned)(n_ktiles * f.Hkv)), dim3(NWB * 64), 0,
-                         stream, a, n_qtiles);
+      hipLaunchKernelGGL(attn_bwd_main_kernel<false>, grid, dim3(NWB * 64), 0, stream, a, n_qtiles, n_units);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
