@@ -257,6 +257,27 @@ def test_bwd_bf16_small(usp, S, Hq, Hkv, lengths, causal):
     check_grad(dv, rv, "dv")
 
 
+def test_bwd_empty_and_invisible(usp):
+    """Calls whose gradients are all zero, written over NaN-filled outputs: no query rows
+    (every key block still writes dK = dV = 0), no keys (dQ = 0), and a ring pair whose
+    keys all lie after its queries (nothing visible)."""
+    say("bwd empty / invisible")
+    S = 1024
+    q, k, v, do, pos = inputs.attention_case(S, 4, 2, 128, seed=9)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    posd = torch.from_numpy(pos).to(DEV)
+    nan = lambda t: torch.full_like(t, float("nan"))
+    cases = (((0, 0), (0, 300)), ((0, 64), (0, 0)), ((0, 256), (512, 1024)))
+    for (qa, qb), (ka, kb) in cases:
+        qs, ks, vs, ds = qd[qa:qb], kd[ka:kb], vd[ka:kb], dod[qa:qb]
+        o, lse = usp.blockattn_fwd(qs, ks, vs, posd, q_start=qa, k_start=ka, causal=True)
+        dq, dk, dv = usp.blockattn_bwd(qs, ks, vs, o, lse, ds, posd, q_start=qa, k_start=ka, causal=True,
+                                       dq=nan(qs), dk=nan(ks), dv=nan(vs))
+        torch.cuda.synchronize()
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            assert torch.all(t == 0), (name, qa, qb, ka, kb)
+
+
 def test_fwd_bwd_causal_4k_full(usp):
     say("bwd causal 4k")
     q, k, v, do, pos = inputs.causal_4k()
