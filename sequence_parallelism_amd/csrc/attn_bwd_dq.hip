@@ -111,6 +111,18 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   for (int kk = 0; kk < 8; ++kk) asm volatile("" :: "v"(qf[kk]), "v"(df[kk]));
   asm volatile("" :: "v"(lse2), "v"(dlt));
   const float sl2 = f.scale * USP_LOG2E;
+  // -D enters dP^T = V dO^T as one more reduction step, fed from registers: A is 1 in
+  // slots 0 and 1 of every key (lanes of half 0), B is (-D_hi, -D_lo) for this lane's
+  // query row with D_hi = bf16(D), D_lo = bf16(D - D_hi), so the product is -D to within
+  // 2^-17 |D| in every element and dS = P (dP - D) needs no subtraction per element
+  bf16x8 one_a = {}, negd_b = {};
+  if (hi == 0) {
+    const bf16 d_hi = (bf16)dlt;
+    one_a[0] = (bf16)1.f;
+    one_a[1] = (bf16)1.f;
+    negd_b[0] = (bf16)(-(float)d_hi);
+    negd_b[1] = (bf16)((float)d_hi - dlt);
+  }
 
   // ---- staging by LDS-DMA: tile u (K, V), load i (0..NL-1) of wave w covers physical
   // chunks [(NW i + w) * 64, +64), lane l the chunk (NW i + w) * 64 + l: key row
@@ -172,6 +184,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
     // of key block kb2 = (i/2)%2, d chunk kk = i/4; the next tile's DMA rides along --
     f32x16 sacc[2], dpacc[2];
     __builtin_amdgcn_s_setprio(2);
+    const f32x16 dinit = mfma32(one_a, negd_b, f32x16{});   // -D in every element
     mfma_pipeline<PF, 32>(
         [&](auto I) {
           constexpr int i = decltype(I)::v, kb2 = (i >> 1) & 1, kk = i >> 2;
@@ -180,7 +193,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
         },
         [&](auto I, const bf16x8& op) {
           constexpr int i = decltype(I)::v, kb2 = (i >> 1) & 1, kk = i >> 2;
-          if constexpr (i & 1) dpacc[kb2] = mfma32(op, df[kk], kk == 0 ? f32x16{} : dpacc[kb2]);
+          if constexpr (i & 1) dpacc[kb2] = mfma32(op, df[kk], kk == 0 ? dinit : dpacc[kb2]);
           else sacc[kb2] = mfma32(op, qf[kk], kk == 0 ? f32x16{} : sacc[kb2]);
         },
         [&](auto I) {
@@ -215,7 +228,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][e], sl2, -lse2));
-        sb[2 * kb2 + (e >> 3)][e & 7] = (bf16)(p * (dpacc[kb2][e] - dlt));
+        sb[2 * kb2 + (e >> 3)][e & 7] = (bf16)(p * dpacc[kb2][e]);   // dP - D
       }
     }
     // ---- dQ^T += K^T dS^T (MFMA i: key chunk c = i/4, head-dim block db = i%4) --------
