@@ -308,8 +308,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_combine_kernel(AttnBwdArgs a,
 
 }  // namespace
 
-// a must carry the workspace regions of attn_bwd_workspace_layout, with D and the
-// head-dim-major k already written (launch_attn_bwd_bf16 does both first).
 // the smallest tile height the launcher uses (sizes the tile-order workspace)
 int attn_bwd_dq_rows_per_tile() { return 128; }
 
@@ -344,6 +342,8 @@ int bwd_dq_split(int64_t Sq, int64_t Sk, int32_t Hq) {
   return (int)std::min<int64_t>(16, (4 * (int64_t)cus + wg - 1) / wg);
 }
 
+// a must carry the workspace regions of attn_bwd_workspace_layout with D already
+// written (launch_attn_bwd_bf16 runs the pre kernel first).
 hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, hipStream_t stream) {
   const AttnArgs& f = a.f;
   if (f.Sq == 0) return hipSuccess;
