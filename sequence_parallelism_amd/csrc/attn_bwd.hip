@@ -43,6 +43,7 @@ constexpr int NWB = 4;              // wavefronts per workgroup
 constexpr int BKV = 32 * NWB;       // keys per workgroup
 constexpr int BQ = 64;              // query rows per item
 constexpr int PF = 4;               // LDS operand reads in flight ahead of their MFMA
+constexpr int NXCD = 8;             // MI355X dispatches workgroup i to XCD i % 8
 constexpr int TILE = BQ * HD;       // elements of one staged tile (16 KB)
 static_assert(TILE / 8 == 4 * NWB * 64, "a staged tile is four 64-lane DMA loads per wave");
 static_assert(BQ == 64, "one lane per query row stages the row scalars");
@@ -72,7 +73,7 @@ __device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const b
 // (row_keys); rows past Sq get 0, 0 and the empty range [KBIG, -KBIG).
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid == 0) *a.kv_next = 0;   // the dK/dV kernel's work queue, which runs after this kernel
+  if (gid < NXCD) a.kv_next[gid] = 0;   // the dK/dV kernel's work queues (it runs after this kernel)
   const int64_t rid = gid >> 4;        // (row, head) pair, 16 lanes each
   const int sub = threadIdx.x & 15;
   const AttnArgs& f = a.f;
@@ -533,19 +534,31 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
   }
 }
 
-// A persistent workgroup per CU takes units from a queue (a.kv_next, zeroed by the pre
-// kernel) in heaviest-first order until none is left.  The hardware would hand the
-// workgroups of a grid to the eight XCDs round-robin, a split fixed at launch; XCDs run
-// at measurably different speeds, and with the queue a slower one simply takes fewer
-// units.
+// A persistent workgroup per CU takes units from per-XCD queues (a.kv_next[8], zeroed
+// by the pre kernel) until none is left.  Unit u belongs to XCD u % 8, the split the
+// hardware's round-robin dispatch of a grid would make: in heaviest-first order the
+// documents interleave, so each XCD works on few documents and their query tiles stay
+// in its L2.  A workgroup takes its own XCD's units (in order) and, once they are gone,
+// those of the other XCDs: XCDs run at measurably different speeds, and a faster one
+// then finishes a slower one's last units.
 template <bool SPLIT>
 __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, int n_qtiles, int n_units) {
   __shared__ __attribute__((aligned(16))) StageBuf stage;
   __shared__ __attribute__((aligned(16))) ScalBuf scal_s;
   __shared__ int unit_s;
+  // this workgroup's XCD (hardware register XCC_ID, bits 0-3)
+  const int xcc = (int)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)) & (NXCD - 1));
   for (;;) {
     __syncthreads();   // the previous unit is done with the LDS (and with unit_s)
-    if (threadIdx.x == 0) unit_s = atomicAdd(a.kv_next, 1);
+    if (threadIdx.x == 0) {
+      int u = n_units;
+      for (int t = 0; t < NXCD; ++t) {   // own queue first; an exhausted queue stays exhausted
+        const int x = (xcc + t) & (NXCD - 1);
+        const int cand = x + NXCD * atomicAdd(&a.kv_next[x], 1);
+        if (cand < n_units) { u = cand; break; }
+      }
+      unit_s = u;
+    }
     __syncthreads();
     const int unit = __builtin_amdgcn_readfirstlane(unit_s);
     if (unit >= n_units) break;   // every wave sees the same unit: all leave together
@@ -608,7 +621,7 @@ size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv,
   size_t n = align256((size_t)Sq * Hq * sizeof(float))                       // D
              + align256((2 * (size_t)Hq + 2) * rs_ld * sizeof(uint32_t))      // row scalars
              + align256(n_kv_blocks(Sk) * sizeof(int))                        // key-block order
-             + align256(sizeof(int))                                          // dK/dV work queue
+             + align256(NXCD * sizeof(int))                                   // dK/dV work queues
              + align256(n_dq_tiles(Sq) * sizeof(int));                        // dQ tile order
   const int qs = bwd_dq_split(Sq, Sk, Hq), ks = bwd_kv_split(Sq, Sk, Hkv);
   if (qs > 1) n += align256((size_t)Hq * (size_t)((Sq + 255) / 256) * qs * 256 * HD * sizeof(float));
@@ -627,7 +640,7 @@ void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
   a.kv_order = reinterpret_cast<int*>(p);
   p += align256(n_kv_blocks(f.Sk) * sizeof(int));
   a.kv_next = reinterpret_cast<int*>(p);
-  p += align256(sizeof(int));
+  p += align256(NXCD * sizeof(int));
   a.dq_order = reinterpret_cast<int*>(p);
   p += align256(n_dq_tiles(f.Sq) * sizeof(int));
   a.dq_split = bwd_dq_split(f.Sq, f.Sk, f.Hq);

@@ -156,7 +156,7 @@ struct AttnBwdArgs {
   uint32_t* rs;
   int32_t rs_ld;
   int* kv_order;       // key blocks of the dK/dV kernel, heaviest first
-  int* kv_next;        // the dK/dV kernel's work queue: next unit to take (zeroed by the pre kernel)
+  int* kv_next;        // the dK/dV kernel's per-XCD work queues [8] (zeroed by the pre kernel)
   int* dq_order;       // query tiles of the dQ kernel, heaviest first
   // split key ranges of the dQ kernel (dq_split > 1): partial dQ^T sums per chunk,
   // dq_part [Hq][tiles][dq_split][256][128] fp32, summed by a combine pass
