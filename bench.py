@@ -310,7 +310,22 @@ def extra_measurements(torch, usp, dev, g):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     res["permute_inverse_full_sp8_GBps"] = round(nbytes / (ms / 1e3) / 1e9, 1)
-    del xs, ys
+    # measured copy ceiling: a plain contiguous device-to-device copy of the same bytes
+    # over the same rotating buffers (cold in the last-level cache, like the permutes)
+    zs = [torch.empty_like(xs[0]) for _ in range(sets)]
+    for i in range(sets):
+        zs[i].copy_(xs[i])
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        zs[i % sets].copy_(xs[i % sets])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    copy_gbps = nbytes / (ms / 1e3) / 1e9
+    res["hbm_copy_measured_GBps"] = round(copy_gbps, 1)
+    res["permute_full_sp8_frac_of_measured_copy"] = round(res["permute_full_sp8_GBps"] / copy_gbps, 4)
+    del xs, ys, zs
 
     blk, H, nb = 16384, 2, 16
     acc = torch.zeros((nb * blk, H, 128), dtype=torch.float32, device=dev)
