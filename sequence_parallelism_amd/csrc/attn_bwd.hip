@@ -114,10 +114,12 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
 }
 
 // ---- 3. main ----------------------------------------------------------------------
-// One work unit: key block kv_order[unit / (Hkv nch)] of key/value head unit % Hkv
-// (units run heaviest first, schedule.hip; the heads of one block are adjacent, then
-// the chunks of a split block).  SPLIT: the unit is chunk c of its key block's items
-// (a.kv_split chunks) and writes its partial dK^T, dV^T sums for the combine pass.
+// One work unit: unit x + NXCD k belongs to XCD x; with m = Hkv nch units per key
+// block, it is key/value head r % Hkv and chunk r / Hkv (r = k % m) of key block
+// kv_order[x + NXCD (k / m)] (schedule.hip: each XCD's blocks form a contiguous key
+// range of equal work, heaviest first; -1 pads a short list).  SPLIT: the unit is
+// chunk c of its key block's items (a.kv_split chunks) and writes its partial dK^T,
+// dV^T sums for the combine pass.
 typedef bf16 StageBuf[2][2 * 64 * 128];   // per buffer: Q [64 rows][128], dO [64][128] (swz16)
 typedef uint32_t ScalBuf[4][2][64];       // per buffer: lse log2(e), -D, klo, khi per row
 template <bool SPLIT>
@@ -127,11 +129,14 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, hi = lane >> 5;
-  const int hk = unit % f.Hkv;
   const int nch = SPLIT ? a.kv_split : 1;
-  const int chunk = SPLIT ? (unit / f.Hkv) % nch : 0;
-  const int n_kb = (f.Sk + BKV - 1) / BKV;              // the order is a permutation of [0, n_kb)
-  const int kbi = min(max(a.kv_order[unit / f.Hkv / nch], 0), n_kb - 1);
+  const int ux = unit % NXCD, uk = unit / NXCD, m = f.Hkv * nch;
+  const int hk = (uk % m) % f.Hkv;
+  const int chunk = SPLIT ? (uk % m) / f.Hkv : 0;
+  const int n_kb = (f.Sk + BKV - 1) / BKV;
+  const int kb_slot = a.kv_order[ux + NXCD * (uk / m)];
+  if (kb_slot < 0) return;                              // padding slot of a short list
+  const int kbi = min(kb_slot, n_kb - 1);
   const int k0 = kbi * BKV;                             // first key
   const int kw0 = k0 + wave * 32;                       // this wave's first key
   const int kl = kw0 + r32;                             // this lane's key (B-operand column)
@@ -248,6 +253,9 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
   const int64_t sc_hstep = wave < 2 ? a.rs_ld : 0;
   auto item_src = [&](int h, int t) {
     ItemSrc r;
+    // the fully visible tiles run from the document end down: the key blocks of one
+    // document (on one XCD) then read the same query tile at about the same time
+    if (t >= f0 && t < f1) t = f0 + f1 - 1 - t;
     const int q0 = t * BQ;
     const int64_t rq = rows_off(f.lq, q0, h) * 2;
     r.tile[0] = reinterpret_cast<const char*>(f.q) + rq;
@@ -279,19 +287,21 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
     scal_s[wave][buf][lane] = p_sc;
   };
 
-  // items run over all heads' fully visible tiles, then over all heads' other tiles;
+  // items run over the fully visible tiles (each tile for every head of the group in
+  // turn), then over all heads' other tiles;
   // (h, t) of items it, it+1, it+2 (the last two clamped to the last item) advance by
   // one item per iteration.  Written with selects only: uniform branches here would
   // cost more than the arithmetic.
   auto next_item = [&](int& h, int& t) {
     const int tn = t + 1;
-    // among the fully visible tiles: wrap to the next head, after the last head to
-    // the first boundary tile of the first head
-    const bool fwrap = tn == f1;
-    const int hf = fwrap ? h + 1 : h;
-    const bool fdone = fwrap && hf == (hk + 1) * grp;
-    const int tf = fdone ? first_masked : (fwrap ? f0 : tn);
-    const int hf2 = fdone ? hk * grp : hf;
+    // among the fully visible tiles the heads run inside the tiles: the next head,
+    // after the last head the next tile, after the last tile the first boundary tile
+    // of the first head
+    const bool hwrap = h + 1 == (hk + 1) * grp;
+    const int tf1 = hwrap ? tn : t;
+    const bool fdone = hwrap && tf1 == f1;
+    const int tf = fdone ? first_masked : tf1;
+    const int hf2 = hwrap ? hk * grp : h + 1;
     // among the boundary tiles [t0, m1) and [m2, t1): skip the gap, then the next head
     const int tm0 = tn == m1 ? m2 : tn;
     const bool mwrap = tm0 >= t1;
@@ -330,9 +340,8 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
   // (h, t) of item `it` in the visiting order (next_item steps through it)
   auto item_at = [&](int it, int& h, int& t) {
     if (it < n_full) {
-      const int nf = f1 - f0;
-      h = hk * grp + it / nf;
-      t = f0 + it % nf;
+      t = f0 + it / grp;
+      h = hk * grp + it % grp;
     } else {
       const int i2 = it - n_full, na = m1 - t0, nm = na + (t1 - m2);
       h = hk * grp + i2 / nm;
@@ -535,33 +544,35 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
 }
 
 // A persistent workgroup per CU takes units from per-XCD queues (a.kv_next[8], zeroed
-// by the pre kernel) until none is left.  Unit u belongs to XCD u % 8, the split the
-// hardware's round-robin dispatch of a grid would make: in heaviest-first order the
-// documents interleave, so each XCD works on few documents and their query tiles stay
-// in its L2.  A workgroup takes its own XCD's units (in order) and, once they are gone,
-// those of the other XCDs: XCDs run at measurably different speeds, and a faster one
-// then finishes a slower one's last units.
+// by the pre kernel) until none is left.  XCD x's units cover one contiguous key range
+// of about an eighth of the work (schedule.hip), so with packed documents an XCD works
+// on few documents and their query tiles stay in its L2.  A workgroup takes its own
+// XCD's units (heaviest first) and, once they are gone, those of the other XCDs: XCDs
+// run at measurably different speeds, and a faster one then finishes a slower one's
+// last units.
 template <bool SPLIT>
-__global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, int n_qtiles, int n_units) {
+__global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, int n_qtiles) {
   __shared__ __attribute__((aligned(16))) StageBuf stage;
   __shared__ __attribute__((aligned(16))) ScalBuf scal_s;
   __shared__ int unit_s;
   // this workgroup's XCD (hardware register XCC_ID, bits 0-3)
   const int xcc = (int)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)) & (NXCD - 1));
+  // units per XCD: the schedule kernel's slots per XCD times the units per key block
+  const int per_xcd = a.kv_slots[0] * a.f.Hkv * (SPLIT ? a.kv_split : 1);
   for (;;) {
     __syncthreads();   // the previous unit is done with the LDS (and with unit_s)
     if (threadIdx.x == 0) {
-      int u = n_units;
+      int u = -1;
       for (int t = 0; t < NXCD; ++t) {   // own queue first; an exhausted queue stays exhausted
         const int x = (xcc + t) & (NXCD - 1);
-        const int cand = x + NXCD * atomicAdd(&a.kv_next[x], 1);
-        if (cand < n_units) { u = cand; break; }
+        const int k = atomicAdd(&a.kv_next[x], 1);
+        if (k < per_xcd) { u = x + NXCD * k; break; }
       }
       unit_s = u;
     }
     __syncthreads();
     const int unit = __builtin_amdgcn_readfirstlane(unit_s);
-    if (unit >= n_units) break;   // every wave sees the same unit: all leave together
+    if (unit < 0) break;   // every wave sees the same unit: all leave together
     attn_bwd_unit<SPLIT>(a, n_qtiles, unit, stage, scal_s);
   }
 }
@@ -620,7 +631,8 @@ size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv,
   const size_t rs_ld = (size_t)((Sq + BQ - 1) / BQ) * BQ;
   size_t n = align256((size_t)Sq * Hq * sizeof(float))                       // D
              + align256((2 * (size_t)Hq + 2) * rs_ld * sizeof(uint32_t))      // row scalars
-             + align256(n_kv_blocks(Sk) * sizeof(int))                        // key-block order
+             + align256(NXCD * n_kv_blocks(Sk) * sizeof(int))                 // key-block order by XCD
+             + align256(sizeof(int))                                          // its slots per XCD
              + align256(NXCD * sizeof(int))                                   // dK/dV work queues
              + align256(n_dq_tiles(Sq) * sizeof(int));                        // dQ tile order
   const int qs = bwd_dq_split(Sq, Sk, Hq), ks = bwd_kv_split(Sq, Sk, Hkv);
@@ -638,7 +650,9 @@ void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
   a.rs = reinterpret_cast<uint32_t*>(p);
   p += align256((2 * (size_t)f.Hq + 2) * (size_t)a.rs_ld * sizeof(uint32_t));
   a.kv_order = reinterpret_cast<int*>(p);
-  p += align256(n_kv_blocks(f.Sk) * sizeof(int));
+  p += align256(NXCD * n_kv_blocks(f.Sk) * sizeof(int));
+  a.kv_slots = reinterpret_cast<int*>(p);
+  p += align256(sizeof(int));
   a.kv_next = reinterpret_cast<int*>(p);
   p += align256(NXCD * sizeof(int));
   a.dq_order = reinterpret_cast<int*>(p);
@@ -671,20 +685,20 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   if (f.Sk > 0) {
     const int n_ktiles = (f.Sk + BKV - 1) / BKV;
     const int n_qtiles = (f.Sq + BQ - 1) / BQ;
-    e = launch_schedule_kv_blocks(f, n_ktiles, BKV, BQ, a.kv_order, stream);
+    e = launch_schedule_kv_blocks(f, n_ktiles, BKV, BQ, a.kv_order, a.kv_slots, stream);
     if (e != hipSuccess) return e;
     // one persistent workgroup per CU (the kernel's registers allow one per CU)
     const int n_units = n_ktiles * f.Hkv * a.kv_split;
     const dim3 grid((unsigned)std::min(n_units, device_cu_count()));
     if (a.kv_split > 1) {
-      hipLaunchKernelGGL(attn_bwd_main_kernel<true>, grid, dim3(NWB * 64), 0, stream, a, n_qtiles, n_units);
+      hipLaunchKernelGGL(attn_bwd_main_kernel<true>, grid, dim3(NWB * 64), 0, stream, a, n_qtiles);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       const int64_t threads = (int64_t)f.Hkv * f.Sk * 16;
       hipLaunchKernelGGL(attn_bwd_kv_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                          stream, a);
     } else {
-      hipLaunchKernelGGL(attn_bwd_main_kernel<false>, grid, dim3(NWB * 64), 0, stream, a, n_qtiles, n_units);
+      hipLaunchKernelGGL(attn_bwd_main_kernel<false>, grid, dim3(NWB * 64), 0, stream, a, n_qtiles);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

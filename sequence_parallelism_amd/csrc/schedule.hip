@@ -8,8 +8,10 @@
 //
 // One workgroup per call: each unit's work (its number of visible tiles) comes from
 // position_ids the same way the kernels derive their tile ranges; units are then
-// bucket-sorted by work, heaviest first, into an int32 order array.  Units of equal
-// bucket keep no particular order; results never depend on the order.
+// bucket-sorted by work, heaviest first, into an int32 order array (the dK/dV kernel's
+// key blocks first grouped into one contiguous key range per XCD).  Units of equal
+// bucket keep no particular order; results never depend on the order beyond fp32
+// summation order.
 #include "common.h"
 
 namespace {
@@ -46,11 +48,8 @@ __device__ int q_tile_work(const AttnArgs& f, int t, int br) {
   return max(hiex1 - lo0, 0);
 }
 
-// KIND 0: key blocks (p0 = keys per block, p1 = rows per query tile, p2 = query tiles);
-// KIND 1: query tiles (p0 = rows per tile).
-template <int KIND>
-__global__ __launch_bounds__(NT) void schedule_kernel(AttnArgs f, int n, int p0, int p1, int p2,
-                                                      int* __restrict__ order) {
+// Query tiles of br rows (forward and dQ kernels), heaviest first.
+__global__ __launch_bounds__(NT) void schedule_q_kernel(AttnArgs f, int n, int br, int* __restrict__ order) {
   __shared__ int w_s[MAXU];
   __shared__ int start[NB];
   __shared__ int wmax_s;
@@ -64,7 +63,7 @@ __global__ __launch_bounds__(NT) void schedule_kernel(AttnArgs f, int n, int p0,
   __syncthreads();
   int wmax = 0;
   for (int u = tid; u < n; u += NT) {
-    const int w = KIND == 0 ? kv_block_work(f, u, p0, p1, p2) : q_tile_work(f, u, p0);
+    const int w = q_tile_work(f, u, br);
     w_s[u] = w;
     wmax = max(wmax, w);
   }
@@ -99,20 +98,121 @@ __global__ __launch_bounds__(NT) void schedule_kernel(AttnArgs f, int n, int p0,
   for (int u = tid; u < n; u += NT) order[atomicAdd(&start[bucket(w_s[u])], 1)] = u;
 }
 
+// Key blocks of the dK/dV kernel, grouped by XCD.  The blocks, in key order, are cut
+// into NXCD contiguous segments of equal total work (with packed documents a segment
+// holds whole documents, so the blocks an XCD runs read the same query tiles from its
+// L2); segment x's blocks, heaviest first, go to slots x, x + NXCD, x + 2 NXCD, ...
+// of `order` (-1 past the segment's end), and slots_out[0] gets the longest segment's
+// length.  `order` holds NXCD * n entries.
+constexpr int NXCD = 8;
+constexpr int NBS = NB / NXCD;   // work buckets per segment
+__global__ __launch_bounds__(NT) void schedule_kv_xcd_kernel(AttnArgs f, int n, int bkv, int bq, int n_qtiles,
+                                                             int* __restrict__ order, int* __restrict__ slots_out) {
+  __shared__ int w_s[MAXU];      // work, then (segment << 27) | work
+  __shared__ int start[NB];
+  __shared__ int64_t part[NT];
+  __shared__ int wmax_s, seg_start[NXCD + 1];
+  const int tid = threadIdx.x;
+  if (n > MAXU) {   // natural order, interleaved over the XCDs
+    const int per = (n + NXCD - 1) / NXCD;
+    for (int u = tid; u < NXCD * per; u += NT) order[u] = u < n ? u : -1;
+    if (tid == 0) slots_out[0] = per;
+    return;
+  }
+  for (int b = tid; b < NB; b += NT) start[b] = 0;
+  if (tid == 0) wmax_s = 0;
+  __syncthreads();
+  // work of the blocks; thread t owns the contiguous blocks [t C, t C + C)
+  const int C = (n + NT - 1) / NT;
+  const int u0 = min(tid * C, n), u1 = min(u0 + C, n);
+  int wmax = 0;
+  int64_t mine = 0;
+  for (int u = u0; u < u1; ++u) {
+    const int w = kv_block_work(f, u, bkv, bq, n_qtiles);
+    w_s[u] = w;
+    wmax = max(wmax, w);
+    mine += w;
+  }
+  atomicMax(&wmax_s, wmax);
+  // inclusive scan of the per-thread sums (Hillis-Steele)
+  part[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {
+    const int64_t add = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  const int64_t total = part[NT - 1];
+  int64_t run = part[tid] - mine;   // work before block u0
+  for (int u = u0; u < u1; ++u) {
+    const int w = w_s[u];
+    // segment of the block's midpoint in the cumulative work (by count when there is none)
+    const int seg = total > 0 ? (int)min<int64_t>(NXCD - 1, ((2 * run + w) * NXCD) / (2 * total))
+                              : (int)(((int64_t)u * NXCD) / n);
+    run += w;
+    w_s[u] = (seg << 27) | w;
+  }
+  __syncthreads();
+  const int64_t wm = max(wmax_s, 1);
+  // bucket: segment-major, then descending work inside the segment
+  auto bucket = [&](int v) {
+    const int seg = v >> 27, w = v & ((1 << 27) - 1);
+    return seg * NBS + (NBS - 1 - (int)(((int64_t)w * (NBS - 1)) / wm));
+  };
+  for (int u = tid; u < n; u += NT) atomicAdd(&start[bucket(w_s[u])], 1);
+  __syncthreads();
+  // exclusive prefix sum of the bucket counts (two buckets per thread)
+  static_assert(NB == 2 * NT, "two buckets per thread");
+  const int c0 = start[2 * tid], c1 = start[2 * tid + 1];
+  int incl = c0 + c1;
+  __syncthreads();
+  start[2 * tid] = incl;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {
+    const int add = tid >= off ? start[2 * (tid - off)] : 0;
+    __syncthreads();
+    incl += add;
+    start[2 * tid] = incl;
+    __syncthreads();
+  }
+  const int excl = incl - c0 - c1;
+  __syncthreads();
+  start[2 * tid] = excl;
+  start[2 * tid + 1] = excl + c0;
+  __syncthreads();
+  if (tid <= NXCD) seg_start[tid] = tid < NXCD ? start[tid * NBS] : n;
+  __syncthreads();
+  int longest = 0;
+#pragma unroll
+  for (int x = 0; x < NXCD; ++x) longest = max(longest, seg_start[x + 1] - seg_start[x]);
+  // padding first (the slots past each segment's end), then the blocks
+  for (int i = tid; i < NXCD * longest; i += NT) {
+    const int x = i % NXCD, k = i / NXCD;
+    if (k >= seg_start[x + 1] - seg_start[x]) order[i] = -1;
+  }
+  for (int u = tid; u < n; u += NT) {
+    const int v = w_s[u], seg = v >> 27;
+    const int pos = atomicAdd(&start[bucket(v)], 1);
+    order[seg + NXCD * (pos - seg_start[seg])] = u;
+  }
+  if (tid == 0) slots_out[0] = longest;
+}
+
 }  // namespace
 
 hipError_t launch_schedule_kv_blocks(const AttnArgs& a, int n_blocks, int bkv, int bq, int* order,
-                                     hipStream_t stream) {
+                                     int* slots_out, hipStream_t stream) {
   if (n_blocks <= 0) return hipSuccess;
   const int n_qtiles = (a.Sq + bq - 1) / bq;
-  hipLaunchKernelGGL(schedule_kernel<0>, dim3(1), dim3(NT), 0, stream, a, n_blocks, bkv, bq, n_qtiles,
-                     order);
+  hipLaunchKernelGGL(schedule_kv_xcd_kernel, dim3(1), dim3(NT), 0, stream, a, n_blocks, bkv, bq, n_qtiles,
+                     order, slots_out);
   return hipGetLastError();
 }
 
 hipError_t launch_schedule_q_tiles(const AttnArgs& a, int n_tiles, int br, int* order,
                                    hipStream_t stream) {
   if (n_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(schedule_kernel<1>, dim3(1), dim3(NT), 0, stream, a, n_tiles, br, 0, 0, order);
+  hipLaunchKernelGGL(schedule_q_kernel, dim3(1), dim3(NT), 0, stream, a, n_tiles, br, order);
   return hipGetLastError();
 }
