@@ -1,4 +1,4 @@
-"""GPU parity of two compositions of the same entry points (the survey's next rows):
+"""GPU parity of two compositions of the same entry points:
 
 * ring backward through the merge: the forward runs query block i against key
   blocks 0..i with fp32 partials merged by lse_merge; the backward then calls
