@@ -317,7 +317,7 @@ hipError_t launch_dq_nw(const AttnBwdArgs& a, hipStream_t stream) {
   constexpr int BR = 32 * NW;
   const AttnArgs& f = a.f;
   const int n_qtiles = (f.Sq + BR - 1) / BR;
-  hipError_t e = launch_schedule_q_tiles(f, n_qtiles, BR, a.dq_order, stream);
+  hipError_t e = launch_schedule_q_tiles(f, n_qtiles, BR, a.dq_order, nullptr, stream);
   if (e != hipSuccess) return e;
   const int nch = SPLIT ? a.dq_split : 1;
   dim3 grid((unsigned)(((n_qtiles + NXCD - 1) / NXCD) * NXCD * f.Hq * nch));

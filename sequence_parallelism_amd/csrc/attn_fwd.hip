@@ -49,34 +49,32 @@ constexpr int TILE = BC * HD;    // elements of one staged tile (16 KB)
 constexpr int NXCD = 8;          // MI355X dispatches workgroup i to XCD i % 8
 
 // NW wavefronts (32 query rows each) per workgroup: 8 normally (one workgroup per
-// CU, 2 waves per SIMD); 4 when a call has too few query tiles to fill the chip
-// with 256-row workgroups (two 128-row workgroups then share a CU).
-// SPLIT: the workgroup takes chunk c of its tile's key range (a.ksplit chunks) and
-// writes a normalised partial O and LSE for the combine pass.
+// CU, 2 waves per SIMD); 4 (one per SIMD, still one workgroup per CU) when a call
+// has too few query tiles to fill the chip with 256-row workgroups.
+// SPLIT: the unit is chunk c of its tile's key range (a.ksplit chunks) and writes a
+// normalised partial O and LSE for the combine pass.
 template <bool O_F32, int NW, bool SPLIT>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int n_qtiles) {
+__device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, int unit,
+                                              bf16 (&stage)[2][2 * TILE], int (&red)[NW][2]) {
   constexpr int BR = 32 * NW;              // query rows per workgroup
   constexpr int NL = TILE / 8 / (NW * 64); // 64-lane DMA loads per wave per staged tile
   static_assert(NL * NW * 64 * 8 == TILE, "a staged tile is a whole number of loads per wave");
-  // per buffer: K [64 keys][128], V [64 keys][128] (swz16)
-  __shared__ __attribute__((aligned(16))) bf16 stage[2][2 * TILE];
-  __shared__ int red[NW][2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, hi = lane >> 5;
-  // XCD-aware order: the workgroups an XCD runs back to back are the query heads
-  // of one query tile (heads sharing a key/value head are adjacent), tiles taken
-  // every NXCD-th in decreasing order of work (schedule.hip), so concurrent
-  // workgroups on an XCD read the same key/value tiles from its L2, every XCD gets a
-  // fair share, and the heaviest tiles start first.
-  // With split key ranges the chunks of a tile follow its heads.
-  const int xcd = blockIdx.x % NXCD, j = blockIdx.x / NXCD;
+  // XCD-aware order: the units of XCD u % NXCD are, in turn, the query heads of one
+  // query tile (heads sharing a key/value head are adjacent), tiles taken every
+  // NXCD-th in decreasing order of work (schedule.hip), so concurrent workgroups on
+  // an XCD read the same key/value tiles from its L2, every XCD gets a fair share,
+  // and the heaviest tiles start first.  With split key ranges the chunks of a tile
+  // follow its heads.
+  const int xcd = unit % NXCD, j = unit / NXCD;
   const int h = j % a.Hq;
   const int nch = SPLIT ? a.ksplit : 1;
   const int chunk = SPLIT ? (j / a.Hq) % nch : 0;
   const int rank = (j / a.Hq / nch) * NXCD + xcd;
-  if (rank >= n_qtiles) return;                             // grid padding (whole workgroup)
+  if (rank >= n_qtiles) return;                             // padding unit (whole workgroup)
   const int qt = min(max(a.q_order[rank], 0), n_qtiles - 1);   // a permutation of the tiles
   const int hk = h / (a.Hq / a.Hkv);
   const int row = qt * BR + wave * 32 + r32;
@@ -291,6 +289,37 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   }
 }
 
+// One persistent workgroup per CU takes units from per-XCD queues (a.q_next[8], zeroed
+// by the schedule kernel that precedes it on the stream): its own XCD's units in order
+// (unit u belongs to XCD u % 8, the hardware's round-robin split, which keeps the query
+// heads of a tile on one XCD), then, once those are gone, the other XCDs' last units,
+// so that a faster XCD finishes a slower one's work.
+template <bool O_F32, int NW, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int n_qtiles, int n_units) {
+  // per buffer: K [64 keys][128], V [64 keys][128] (swz16)
+  __shared__ __attribute__((aligned(16))) bf16 stage[2][2 * TILE];
+  __shared__ int red[NW][2];
+  __shared__ int unit_s;
+  const int xcc = (int)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)) & (NXCD - 1));   // XCC_ID
+  const int per_xcd = (n_units + NXCD - 1) / NXCD;
+  for (;;) {
+    __syncthreads();   // the previous unit is done with the LDS (and with unit_s)
+    if (threadIdx.x == 0) {
+      int u = -1;
+      for (int t = 0; t < NXCD; ++t) {   // own queue first; an exhausted queue stays exhausted
+        const int x = (xcc + t) & (NXCD - 1);
+        const int k = atomicAdd(&a.q_next[x], 1);
+        if (k < per_xcd) { u = x + NXCD * k; break; }
+      }
+      unit_s = u;
+    }
+    __syncthreads();
+    const int unit = __builtin_amdgcn_readfirstlane(unit_s);
+    if (unit < 0) break;   // every wave sees the same unit: all leave together
+    attn_fwd_unit<O_F32, NW, SPLIT>(a, n_qtiles, unit, stage, red);
+  }
+}
+
 // ---- combine of split key ranges: per (head, row), the cumulative-softmax merge of
 // its tile's chunk partials (as lse_merge, over ksplit parts) -------------------------
 template <bool O_F32, int BR>
@@ -390,12 +419,12 @@ int fwd_ksplit(int64_t Sq, int64_t Sk, int32_t Hq) {
 }
 
 // workspace: the query-tile order (sized for the 128-row tiles of the 4-wave
-// variant), and with a key-range split the partials
+// variant), the per-XCD work queues, and with a key-range split the partials
 // o_part [Hq][tiles][ksplit][256][128] and lse_part [Hq][tiles][ksplit][256] (fp32)
 size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D, int bf16_path) {
   if (!bf16_path) return 0;
   const size_t n_qtiles = (size_t)((Sq + 127) / 128);
-  size_t n = align256(n_qtiles * sizeof(int));
+  size_t n = align256(n_qtiles * sizeof(int)) + align256(NXCD * sizeof(int));
   const int ks = fwd_ksplit(Sq, Sk, Hq);
   if (ks > 1) {
     const size_t slots = (size_t)Hq * (size_t)((Sq + 255) / 256) * ks;
@@ -408,6 +437,8 @@ void attn_fwd_workspace_layout(AttnArgs& a, void* base) {
   char* p = reinterpret_cast<char*>(base);
   a.q_order = reinterpret_cast<int*>(p);
   p += align256((size_t)((a.Sq + 127) / 128) * sizeof(int));
+  a.q_next = reinterpret_cast<int*>(p);
+  p += align256(NXCD * sizeof(int));
   a.ksplit = fwd_ksplit(a.Sq, a.Sk, a.Hq);
   if (a.ksplit > 1) {
     const size_t slots = (size_t)a.Hq * (size_t)((a.Sq + 255) / 256) * a.ksplit;
@@ -422,14 +453,17 @@ template <int NW, bool SPLIT>
 hipError_t launch_fwd_nw(const AttnArgs& a, int o_f32, hipStream_t stream) {
   constexpr int BR = 32 * NW;
   const int n_qtiles = (a.Sq + BR - 1) / BR;
-  hipError_t e = launch_schedule_q_tiles(a, n_qtiles, BR, a.q_order, stream);
+  hipError_t e = launch_schedule_q_tiles(a, n_qtiles, BR, a.q_order, a.q_next, stream);
   if (e != hipSuccess) return e;
   const int nch = SPLIT ? a.ksplit : 1;
-  dim3 grid((unsigned)(((n_qtiles + NXCD - 1) / NXCD) * NXCD * a.Hq * nch));
+  // units: (tile rank, head, chunk), the ranks padded to a multiple of NXCD
+  const int n_units = ((n_qtiles + NXCD - 1) / NXCD) * NXCD * a.Hq * nch;
+  // one persistent workgroup per CU (the kernel's registers allow no more)
+  const dim3 grid((unsigned)std::min(n_units, device_cu_count()));
   if (o_f32)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<true, NW, SPLIT>), grid, dim3(NW * 64), 0, stream, a, n_qtiles);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<true, NW, SPLIT>), grid, dim3(NW * 64), 0, stream, a, n_qtiles, n_units);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, NW, SPLIT>), grid, dim3(NW * 64), 0, stream, a, n_qtiles);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, NW, SPLIT>), grid, dim3(NW * 64), 0, stream, a, n_qtiles, n_units);
   e = hipGetLastError();
   if constexpr (SPLIT) {
     if (e != hipSuccess) return e;

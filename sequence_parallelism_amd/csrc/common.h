@@ -92,6 +92,7 @@ struct AttnArgs {
   int32_t causal;
   float scale;
   int* q_order;        // bf16 path: query tiles heaviest first (schedule.hip)
+  int* q_next;         // bf16 path: the forward kernel's per-XCD work queues [8]
   // bf16 forward with split key ranges (ksplit > 1): each query tile's visible keys
   // are cut into ksplit chunks, one workgroup each, whose normalised partial O and
   // LSE go to o_part [Hq][tiles][ksplit][256][128] and lse_part [Hq][tiles][ksplit][256]
@@ -186,7 +187,8 @@ int attn_bwd_dq_rows_per_tile();
 // key blocks grouped by XCD (order: NXCD * n_blocks entries; slots_out[0]: slots per XCD)
 hipError_t launch_schedule_kv_blocks(const AttnArgs& a, int n_blocks, int bkv, int bq, int* order, int* slots_out,
                                      hipStream_t s);
-hipError_t launch_schedule_q_tiles(const AttnArgs& a, int n_tiles, int br, int* order, hipStream_t s);
+// (q_next: NULL, or NXCD work-queue counters that the launch also zeroes)
+hipError_t launch_schedule_q_tiles(const AttnArgs& a, int n_tiles, int br, int* order, int* q_next, hipStream_t s);
 
 
 struct MergeArgs {

@@ -49,11 +49,13 @@ __device__ int q_tile_work(const AttnArgs& f, int t, int br) {
 }
 
 // Query tiles of br rows (forward and dQ kernels), heaviest first.
-__global__ __launch_bounds__(NT) void schedule_q_kernel(AttnArgs f, int n, int br, int* __restrict__ order) {
+__global__ __launch_bounds__(NT) void schedule_q_kernel(AttnArgs f, int n, int br, int* __restrict__ order,
+                                                        int* __restrict__ q_next) {
   __shared__ int w_s[MAXU];
   __shared__ int start[NB];
   __shared__ int wmax_s;
   const int tid = threadIdx.x;
+  if (q_next && tid < 8) q_next[tid] = 0;   // the work queues of the kernel that follows
   if (n > MAXU) {
     for (int u = tid; u < n; u += NT) order[u] = u;
     return;
@@ -210,9 +212,9 @@ hipError_t launch_schedule_kv_blocks(const AttnArgs& a, int n_blocks, int bkv, i
   return hipGetLastError();
 }
 
-hipError_t launch_schedule_q_tiles(const AttnArgs& a, int n_tiles, int br, int* order,
+hipError_t launch_schedule_q_tiles(const AttnArgs& a, int n_tiles, int br, int* order, int* q_next,
                                    hipStream_t stream) {
   if (n_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(schedule_q_kernel, dim3(1), dim3(NT), 0, stream, a, n_tiles, br, order);
+  hipLaunchKernelGGL(schedule_q_kernel, dim3(1), dim3(NT), 0, stream, a, n_tiles, br, order, q_next);
   return hipGetLastError();
 }

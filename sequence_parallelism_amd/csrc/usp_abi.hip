@@ -65,6 +65,7 @@ AttnArgs make_args(const void* q, const void* k, const void* v, int64_t Sq, int6
   a.causal = causal ? 1 : 0;
   a.scale = scale;
   a.q_order = nullptr;
+  a.q_next = nullptr;
   a.ksplit = 1;
   a.o_part = nullptr;
   a.lse_part = nullptr;
