@@ -6,7 +6,9 @@
 // with dK, dV of a key/value head summed over the query heads that share it.
 //
 // Kernels, in stream order:
-//   1. pre:       D_i for every (row, head);
+//   1. dQ:        attn_bwd_dq.hip, query-stationary, recomputing S and dP (no atomics);
+//                 it forms D_i from the dO and O rows it holds and writes the row
+//                 scalars of the dK/dV kernel (lse log2 e, -D, the visible keys);
 //   2. dK, dV:    a workgroup owns 128 keys of one key/value head (32 per wave; K
 //                 and V of the lane's key are B operands in registers) and walks the
 //                 64-row query tiles that can see the block, for every query head of
@@ -23,8 +25,7 @@
 //                 and after every MFMA it issues one piece of independent work that
 //                 the matrix core's execution hides: the next item's DMA (spread over
 //                 the whole item), and P and dS of the previous 32 rows (exp2,
-//                 products, bf16 packing);
-//   3. dQ:        attn_bwd_dq.hip, query-stationary, recomputing S and dP (no atomics).
+//                 products, bf16 packing).
 // Query tiles that cannot see the key block are not visited (the first visible
 // tile follows from the block's first key, the last from a binary search over
 // document starts).  Fully visible tiles run first, without any masking work; the
@@ -67,53 +68,7 @@ __device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const b
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-// ---- 1. D = rowsum(dO * O), and the row scalars of the dK/dV kernel -----------------
-// For every (row, head) with row < rs_ld (Sq rounded up to the 64-row tile): D, and in
-// the planes of a.rs lse log2(e), -D, and (head 0) the row's visible keys [klo, khi)
-// (row_keys); rows past Sq get 0, 0 and the empty range [KBIG, -KBIG).
-__global__ __launch_bounds__(256) void attn_bwd_pre_kernel(AttnBwdArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid < NXCD) a.kv_next[gid] = 0;   // the dK/dV kernel's work queues (it runs after this kernel)
-  const int64_t rid = gid >> 4;        // (row, head) pair, 16 lanes each
-  const int sub = threadIdx.x & 15;
-  const AttnArgs& f = a.f;
-  if (rid >= (int64_t)a.rs_ld * f.Hq) return;
-  const int row = (int)(rid / f.Hq);
-  const int h = (int)(rid - (int64_t)row * f.Hq);
-  const int64_t ld = a.rs_ld;
-  float* lse2p = reinterpret_cast<float*>(a.rs) + (int64_t)h * ld + row;
-  float* ndp = reinterpret_cast<float*>(a.rs) + ((int64_t)f.Hq + h) * ld + row;
-  int* klop = reinterpret_cast<int*>(a.rs) + 2 * (int64_t)f.Hq * ld + row;
-  int* khip = klop + ld;
-  if (row >= f.Sq) {   // padding rows: no work, an empty key range
-    if (sub == 0) *lse2p = 0.f;
-    if (sub == 1) *ndp = 0.f;
-    if (h == 0 && sub == 2) *klop = KBIG;
-    if (h == 0 && sub == 3) *khip = -KBIG;
-    return;
-  }
-  const int64_t off = rows_off(f.lq, row, h) + sub * 8;
-  const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(f.o) + off);
-  const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.dout) + off);
-  float acc = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc += (float)o8[j] * (float)d8[j];
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (sub == 0) {
-    a.delta[(int64_t)h * f.Sq + row] = acc;
-    *lse2p = f.lse[(int64_t)h * f.lse_ld + row] * USP_LOG2E;
-  }
-  if (sub == 1) *ndp = -acc;
-  if (h == 0 && sub == 2) {
-    int lo, hiex;
-    row_keys(f, row, lo, hiex);
-    *klop = lo;
-    *khip = hiex;
-  }
-}
-
-// ---- 3. main ----------------------------------------------------------------------
+// ---- 2. main ----------------------------------------------------------------------
 // One work unit: unit x + NXCD k belongs to XCD x; with m = Hkv nch units per key
 // block, it is key/value head r % Hkv and chunk r / Hkv (r = k % m) of key block
 // kv_order[x + NXCD (k / m)] (schedule.hip: each XCD's blocks form a contiguous key
@@ -274,7 +229,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
     dma16(src.tile[u], vq, __builtin_amdgcn_readfirstlane(lds));
   };
 
-  // Row scalars of an item (made by the pre kernel), one row per lane, read one item
+  // Row scalars of an item (written by the dQ kernel), one row per lane, read one item
   // ahead: wave w loads plane w, with no arithmetic on the value (that would stall the
   // pipeline it sits in for a whole memory latency), and stores it at the item's
   // publishing barrier.
@@ -544,7 +499,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
 }
 
 // A persistent workgroup per CU takes units from per-XCD queues (a.kv_next[8], zeroed
-// by the pre kernel) until none is left.  XCD x's units cover one contiguous key range
+// by the schedule kernel) until none is left.  XCD x's units cover one contiguous key range
 // of about an eighth of the work (schedule.hip), so with packed documents an XCD works
 // on few documents and their query tiles stay in its L2.  A workgroup takes its own
 // XCD's units (heaviest first) and, once they are gone, those of the other XCDs: XCDs
@@ -629,8 +584,7 @@ int bwd_kv_split(int64_t Sq, int64_t Sk, int32_t Hkv) {
 
 size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D) {
   const size_t rs_ld = (size_t)((Sq + BQ - 1) / BQ) * BQ;
-  size_t n = align256((size_t)Sq * Hq * sizeof(float))                       // D
-             + align256((2 * (size_t)Hq + 2) * rs_ld * sizeof(uint32_t))      // row scalars
+  size_t n = align256((2 * (size_t)Hq + 2) * rs_ld * sizeof(uint32_t))        // row scalars
              + align256(NXCD * n_kv_blocks(Sk) * sizeof(int))                 // key-block order by XCD
              + align256(sizeof(int))                                          // its slots per XCD
              + align256(NXCD * sizeof(int))                                   // dK/dV work queues
@@ -644,8 +598,6 @@ size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv,
 void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
   const AttnArgs& f = a.f;
   char* p = reinterpret_cast<char*>(base);
-  a.delta = reinterpret_cast<float*>(p);
-  p += align256((size_t)f.Sq * f.Hq * sizeof(float));
   a.rs_ld = ((f.Sq + BQ - 1) / BQ) * BQ;
   a.rs = reinterpret_cast<uint32_t*>(p);
   p += align256((2 * (size_t)f.Hq + 2) * (size_t)a.rs_ld * sizeof(uint32_t));
@@ -676,32 +628,25 @@ bool attn_bwd_supported(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv) {
 
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   const AttnArgs& f = a.f;
-  // at least one workgroup: the pre kernel also resets the dK/dV kernel's queue
-  const int64_t rows = (int64_t)a.rs_ld * f.Hq;
-  hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)std::max<int64_t>(1, (rows * 16 + 255) / 256)), dim3(256), 0,
-                     stream, a);
-  hipError_t e = hipGetLastError();
+  // dQ first: it also writes the row scalars the dK/dV kernel reads
+  hipError_t e = launch_attn_bwd_dq(a, stream);
+  if (e != hipSuccess || f.Sk == 0) return e;
+  const int n_ktiles = (f.Sk + BKV - 1) / BKV;
+  const int n_qtiles = (f.Sq + BQ - 1) / BQ;
+  e = launch_schedule_kv_blocks(f, n_ktiles, BKV, BQ, a.kv_order, a.kv_slots, a.kv_next, stream);
   if (e != hipSuccess) return e;
-  if (f.Sk > 0) {
-    const int n_ktiles = (f.Sk + BKV - 1) / BKV;
-    const int n_qtiles = (f.Sq + BQ - 1) / BQ;
-    e = launch_schedule_kv_blocks(f, n_ktiles, BKV, BQ, a.kv_order, a.kv_slots, stream);
-    if (e != hipSuccess) return e;
-    // one persistent workgroup per CU (the kernel's registers allow one per CU)
-    const int n_units = n_ktiles * f.Hkv * a.kv_split;
-    const dim3 grid((unsigned)std::min(n_units, device_cu_count()));
-    if (a.kv_split > 1) {
-      hipLaunchKernelGGL(attn_bwd_main_kernel<true>, grid, dim3(NWB * 64), 0, stream, a, n_qtiles);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      const int64_t threads = (int64_t)f.Hkv * f.Sk * 16;
-      hipLaunchKernelGGL(attn_bwd_kv_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                         stream, a);
-    } else {
-      hipLaunchKernelGGL(attn_bwd_main_kernel<false>, grid, dim3(NWB * 64), 0, stream, a, n_qtiles);
-    }
+  // one persistent workgroup per CU (the kernel's registers allow one per CU)
+  const int n_units = n_ktiles * f.Hkv * a.kv_split;
+  const dim3 grid((unsigned)std::min(n_units, device_cu_count()));
+  if (a.kv_split > 1) {
+    hipLaunchKernelGGL(attn_bwd_main_kernel<true>, grid, dim3(NWB * 64), 0, stream, a, n_qtiles);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const int64_t threads = (int64_t)f.Hkv * f.Sk * 16;
+    hipLaunchKernelGGL(attn_bwd_kv_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL(attn_bwd_main_kernel<false>, grid, dim3(NWB * 64), 0, stream, a, n_qtiles);
   }
-  return launch_attn_bwd_dq(a, stream);
+  return hipGetLastError();
 }

@@ -83,47 +83,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
     ke = min(ke, kb + len);
   }
 
-  // ---- Q and dO fragments (B operands of S^T = K Q^T, dP^T = V dO^T):
-  // row r32, d = 16 kk + 8 hi + 0..7 ------------------------------------------------
-  bf16x8 qf[8], df[8];
-  {
-    const int64_t off = rows_off(f.lq, row_ok ? row : 0, h) + 8 * hi;
-    const bf16* qsrc = reinterpret_cast<const bf16*>(f.q) + off;
-    const bf16* dsrc = reinterpret_cast<const bf16*>(a.dout) + off;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      bf16x8 z = {};
-      qf[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(qsrc + 16 * kk) : z;
-      df[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(dsrc + 16 * kk) : z;
-    }
-  }
-  // row scalars: lse in log2 units (+inf for a row with no visible key, so that P = 0
-  // there) and D
-  float lse2 = INFINITY, dlt = 0.f;
-  if (row_ok) {
-    const float l = f.lse[(int64_t)h * f.lse_ld + row];
-    lse2 = l == -INFINITY ? INFINITY : l * USP_LOG2E;
-    dlt = a.delta[(int64_t)h * f.Sq + row];
-  }
-  // consumed here, so that the compiler waits for these loads once, now, and not
-  // inside the tile loop (where its wait would also cover the tile DMA in flight)
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) asm volatile("" :: "v"(qf[kk]), "v"(df[kk]));
-  asm volatile("" :: "v"(lse2), "v"(dlt));
-  const float sl2 = f.scale * USP_LOG2E;
-  // -D enters dP^T = V dO^T as one more reduction step, fed from registers: A is 1 in
-  // slots 0 and 1 of every key (lanes of half 0), B is (-D_hi, -D_lo) for this lane's
-  // query row with D_hi = bf16(D), D_lo = bf16(D - D_hi), so the product is -D to within
-  // 2^-17 |D| in every element and dS = P (dP - D) needs no subtraction per element
-  bf16x8 one_a = {}, negd_b = {};
-  if (hi == 0) {
-    const bf16 d_hi = (bf16)dlt;
-    one_a[0] = (bf16)1.f;
-    one_a[1] = (bf16)1.f;
-    negd_b[0] = (bf16)(-(float)d_hi);
-    negd_b[1] = (bf16)((float)d_hi - dlt);
-  }
-
   // ---- staging by LDS-DMA: tile u (K, V), load i (0..NL-1) of wave w covers physical
   // chunks [(NW i + w) * 64, +64), lane l the chunk (NW i + w) * 64 + l: key row
   // 4 NW i + 4w + l/16, physical chunk l%16.  The swizzle depends on the row modulo 16
@@ -168,8 +127,83 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
 #pragma unroll
   for (int i = 0; i < 4; ++i) dqacc[i] = f32x16{};
 
-  if (kb < ke) {
+  // the first tile's DMA goes out before the fragment loads, so the two latencies overlap
+  if (kb < ke)
     for (int s = 0; s < 2 * NL; ++s) dma_step(s, kb, 0);
+
+  // ---- Q and dO fragments (B operands of S^T = K Q^T, dP^T = V dO^T):
+  // row r32, d = 16 kk + 8 hi + 0..7 ------------------------------------------------
+  // (a row past Sq reads row 0 and is inert: its lse is +inf, so P = dS = 0, and its
+  // dQ is not stored; no per-lane select, which would make the loads wait one by one)
+  bf16x8 qf[8], df[8];
+  {
+    const int64_t off = rows_off(f.lq, row_ok ? row : 0, h) + 8 * hi;
+    const bf16* qsrc = reinterpret_cast<const bf16*>(f.q) + off;
+    const bf16* dsrc = reinterpret_cast<const bf16*>(a.dout) + off;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      qf[kk] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * kk);
+      df[kk] = *reinterpret_cast<const bf16x8*>(dsrc + 16 * kk);
+    }
+  }
+  // row scalars: lse in log2 units (+inf for a row with no visible key, so that P = 0
+  // there) and D = <dO, O> over the row, from the lane's dO fragments and the O
+  // elements at the same places (fp32 dot products of bf16 pairs; the lane 32 apart
+  // holds the other half of the row)
+  float l_raw = 0.f, dlt = 0.f;
+  {
+    const bf16* osrc = reinterpret_cast<const bf16*>(f.o) + rows_off(f.lq, row_ok ? row : 0, h) + 8 * hi;
+    bf16x8 of[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      of[kk] = *reinterpret_cast<const bf16x8*>(osrc + 16 * kk);
+    }
+    if (row_ok) l_raw = f.lse[(int64_t)h * f.lse_ld + row];
+    auto dot2 = [](const bf16x2 x, const bf16x2 y, float c) { return __builtin_amdgcn_fdot2_f32_bf16(x, y, c, false); };
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8 d = df[kk], o = of[kk];
+      dlt = dot2(__builtin_shufflevector(d, d, 0, 1), __builtin_shufflevector(o, o, 0, 1), dlt);
+      dlt = dot2(__builtin_shufflevector(d, d, 2, 3), __builtin_shufflevector(o, o, 2, 3), dlt);
+      dlt = dot2(__builtin_shufflevector(d, d, 4, 5), __builtin_shufflevector(o, o, 4, 5), dlt);
+      dlt = dot2(__builtin_shufflevector(d, d, 6, 7), __builtin_shufflevector(o, o, 6, 7), dlt);
+    }
+    dlt += __shfl_xor(dlt, 32);
+  }
+  const float lse2 = row_ok ? (l_raw == -INFINITY ? INFINITY : l_raw * USP_LOG2E) : INFINITY;
+  // the dK/dV kernel's row scalars (it runs after this kernel), once per (row, head):
+  // lse log2(e), -D and, for head 0, the row's visible keys; rows past Sq up to the
+  // planes' 64-row padding get 0, 0 and the empty range [KBIG, -KBIG)
+  if (hi == 0 && chunk == 0 && row < a.rs_ld) {
+    const int64_t ld = a.rs_ld;
+    reinterpret_cast<float*>(a.rs)[(int64_t)h * ld + row] = row_ok ? l_raw * USP_LOG2E : 0.f;
+    reinterpret_cast<float*>(a.rs)[((int64_t)f.Hq + h) * ld + row] = row_ok ? -dlt : 0.f;
+    if (h == 0) {
+      int* klop = reinterpret_cast<int*>(a.rs) + 2 * (int64_t)f.Hq * ld + row;
+      klop[0] = row_ok ? klo : KBIG;
+      klop[ld] = row_ok ? khi : -KBIG;
+    }
+  }
+  // consumed here, so that the compiler waits for these loads once, now, and not
+  // inside the tile loop (where its wait would also cover the tile DMA in flight)
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) asm volatile("" :: "v"(qf[kk]), "v"(df[kk]));
+  asm volatile("" :: "v"(lse2), "v"(dlt));
+  const float sl2 = f.scale * USP_LOG2E;
+  // -D enters dP^T = V dO^T as one more reduction step, fed from registers: A is 1 in
+  // slots 0 and 1 of every key (lanes of half 0), B is (-D_hi, -D_lo) for this lane's
+  // query row with D_hi = bf16(D), D_lo = bf16(D - D_hi), so the product is -D to within
+  // 2^-17 |D| in every element and dS = P (dP - D) needs no subtraction per element
+  bf16x8 one_a = {}, negd_b = {};
+  if (hi == 0) {
+    const bf16 d_hi = (bf16)dlt;
+    one_a[0] = (bf16)1.f;
+    one_a[1] = (bf16)1.f;
+    negd_b[0] = (bf16)(-(float)d_hi);
+    negd_b[1] = (bf16)((float)d_hi - dlt);
+  }
+
+  if (kb < ke) {
     wait_vmem();
     __syncthreads();
   }
@@ -342,8 +376,9 @@ int bwd_dq_split(int64_t Sq, int64_t Sk, int32_t Hq) {
   return (int)std::min<int64_t>(16, (4 * (int64_t)cus + wg - 1) / wg);
 }
 
-// a must carry the workspace regions of attn_bwd_workspace_layout with D already
-// written (launch_attn_bwd_bf16 runs the pre kernel first).
+// a must carry the workspace regions of attn_bwd_workspace_layout; the kernel also
+// writes the row scalars that the dK/dV kernel reads (launch_attn_bwd_bf16 runs it
+// first).
 hipError_t launch_attn_bwd_dq(const AttnBwdArgs& a, hipStream_t stream) {
   const AttnArgs& f = a.f;
   if (f.Sq == 0) return hipSuccess;

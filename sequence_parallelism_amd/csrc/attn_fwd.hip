@@ -102,21 +102,6 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
     ke = min(ke, kb + len);
   }
 
-  // ---- Q fragment (B operand of S^T = K Q^T): row r32, d = 16*kk + 8*hi + 0..7
-  bf16x8 qf[8];
-  {
-    const bf16* src = qp + rows_off(a.lq, row_ok ? row : 0, h) + 8 * hi;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      bf16x8 z = {};
-      qf[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(src + 16 * kk) : z;
-    }
-    // consumed here, so that the compiler waits for these loads once, now, and not
-    // inside the tile loop (where its wait would also cover the tile DMA in flight)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) asm volatile("" :: "v"(qf[kk]));
-  }
-
   // ---- staging by LDS-DMA: tile u (K, V), load i (0..NL-1) of wave w covers physical
   // chunks [(NW i + w) * 64, +64), lane l the chunk (NW i + w) * 64 + l: key row
   // 4 NW i + 4w + l/16, physical chunk l%16.  The swizzle depends on the row modulo 16
@@ -163,8 +148,26 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
     }
   }
 
-  if (kb < ke) {
+  // the first tile's DMA goes out before the fragment loads, so the two latencies overlap
+  if (kb < ke)
     for (int s = 0; s < 2 * NL; ++s) dma_step(s, kb, 0);
+
+  // ---- Q fragment (B operand of S^T = K Q^T): row r32, d = 16*kk + 8*hi + 0..7
+  // (a row past Sq reads row 0; its results are not stored)
+  bf16x8 qf[8];
+  {
+    const bf16* src = qp + rows_off(a.lq, row_ok ? row : 0, h) + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      qf[kk] = *reinterpret_cast<const bf16x8*>(src + 16 * kk);
+    }
+    // consumed here, so that the compiler waits for these loads once, now, and not
+    // inside the tile loop (where its wait would also cover the tile DMA in flight)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) asm volatile("" :: "v"(qf[kk]));
+  }
+
+  if (kb < ke) {
     wait_vmem();
     __syncthreads();
   }

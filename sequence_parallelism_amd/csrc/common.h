@@ -151,14 +151,13 @@ struct AttnBwdArgs {
   void* dk;
   void* dv;
   // workspace regions
-  float* delta;        // [Hq][Sq] fp32
   // row scalars of the dK/dV kernel, planes of rs_ld (Sq rounded up to 64) rows:
   // [Hq] lse log2(e), [Hq] -D (fp32 bits), then klo, khi (int32, the visible keys)
   uint32_t* rs;
   int32_t rs_ld;
   int* kv_order;       // key blocks of the dK/dV kernel by XCD: slot x + 8 i = XCD x's i-th (-1: none)
   int* kv_slots;       // [1]: slots per XCD in kv_order (written by the schedule kernel)
-  int* kv_next;        // the dK/dV kernel's per-XCD work queues [8] (zeroed by the pre kernel)
+  int* kv_next;        // the dK/dV kernel's per-XCD work queues [8] (zeroed by its schedule kernel)
   int* dq_order;       // query tiles of the dQ kernel, heaviest first
   // split key ranges of the dQ kernel (dq_split > 1): partial dQ^T sums per chunk,
   // dq_part [Hq][tiles][dq_split][256][128] fp32, summed by a combine pass
@@ -184,9 +183,10 @@ int attn_bwd_dq_rows_per_tile();
 
 // Heaviest-first launch orders (schedule.hip): key blocks of bkv keys seen by bq-row
 // query tiles (dK/dV kernel), and query tiles of br rows (forward and dQ kernels).
-// key blocks grouped by XCD (order: NXCD * n_blocks entries; slots_out[0]: slots per XCD)
+// key blocks grouped by XCD (order: NXCD * n_blocks entries; slots_out[0]: slots per XCD;
+// and NXCD work-queue counters `next` that the launch zeroes)
 hipError_t launch_schedule_kv_blocks(const AttnArgs& a, int n_blocks, int bkv, int bq, int* order, int* slots_out,
-                                     hipStream_t s);
+                                     int* next, hipStream_t s);
 // (q_next: NULL, or NXCD work-queue counters that the launch also zeroes)
 hipError_t launch_schedule_q_tiles(const AttnArgs& a, int n_tiles, int br, int* order, int* q_next, hipStream_t s);
 

@@ -105,16 +105,19 @@ __global__ __launch_bounds__(NT) void schedule_q_kernel(AttnArgs f, int n, int b
 // holds whole documents, so the blocks an XCD runs read the same query tiles from its
 // L2); segment x's blocks, heaviest first, go to slots x, x + NXCD, x + 2 NXCD, ...
 // of `order` (-1 past the segment's end), and slots_out[0] gets the longest segment's
-// length.  `order` holds NXCD * n entries.
+// length.  `order` holds NXCD * n entries; next[0..7], the work queues of the kernel
+// that follows, are zeroed.
 constexpr int NXCD = 8;
 constexpr int NBS = NB / NXCD;   // work buckets per segment
 __global__ __launch_bounds__(NT) void schedule_kv_xcd_kernel(AttnArgs f, int n, int bkv, int bq, int n_qtiles,
-                                                             int* __restrict__ order, int* __restrict__ slots_out) {
+                                                             int* __restrict__ order, int* __restrict__ slots_out,
+                                                             int* __restrict__ next) {
   __shared__ int w_s[MAXU];      // work, then (segment << 27) | work
   __shared__ int start[NB];
   __shared__ int64_t part[NT];
   __shared__ int wmax_s, seg_start[NXCD + 1];
   const int tid = threadIdx.x;
+  if (tid < NXCD) next[tid] = 0;
   if (n > MAXU) {   // natural order, interleaved over the XCDs
     const int per = (n + NXCD - 1) / NXCD;
     for (int u = tid; u < NXCD * per; u += NT) order[u] = u < n ? u : -1;
@@ -204,11 +207,11 @@ __global__ __launch_bounds__(NT) void schedule_kv_xcd_kernel(AttnArgs f, int n, 
 }  // namespace
 
 hipError_t launch_schedule_kv_blocks(const AttnArgs& a, int n_blocks, int bkv, int bq, int* order,
-                                     int* slots_out, hipStream_t stream) {
+                                     int* slots_out, int* next, hipStream_t stream) {
   if (n_blocks <= 0) return hipSuccess;
   const int n_qtiles = (a.Sq + bq - 1) / bq;
   hipLaunchKernelGGL(schedule_kv_xcd_kernel, dim3(1), dim3(NT), 0, stream, a, n_blocks, bkv, bq, n_qtiles,
-                     order, slots_out);
+                     order, slots_out, next);
   return hipGetLastError();
 }
 
