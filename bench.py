@@ -240,8 +240,8 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(dominant),
-                "kernel": "usp_ulysses_attn_bwd call: D pre-pass, launch-order schedules, dK/dV kernel, "
-                          "dQ kernel" if dominant == "bwd"
+                "kernel": "usp_ulysses_attn_bwd call: launch-order schedules, dQ kernel (also D and the "
+                          "row scalars), dK/dV kernel" if dominant == "bwd"
                 else "usp_ulysses_attn_fwd call: launch-order schedule, attention kernel"}
 
     if args.calib_copy:
