@@ -20,9 +20,33 @@ constexpr int NT = 1024;        // threads of the one workgroup
 constexpr int NB = 2048;        // work buckets
 constexpr int MAXU = 12288;     // units sorted in LDS; larger launches keep natural order
 
+constexpr int MAXT = 8192;
+constexpr int NWAVE = NT / 64;
+
+// Inclusive prefix sum of v over the workgroup's NT threads in thread order: a scan
+// inside each wavefront by shuffles, then the totals of the wavefronts before it
+// (two barriers in all).  wsum: NWAVE entries of LDS.
+template <typename T>
+__device__ T block_incl_scan(T v, T* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const T y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  T before = 0;
+  for (int i = 0; i < w; ++i) before += wsum[i];
+  __syncthreads();   // wsum may be reused
+  return v + before;
+}      // query tiles whose first visible key the dK/dV schedule keeps in LDS
+
 // Work of key block b of BKV keys for the dK/dV kernel: the number of BQ-row query
 // tiles that can see it (the kernel visits these for every query head of the group).
-__device__ int kv_block_work(const AttnArgs& f, int b, int bkv, int bq, int n_qtiles) {
+// tile_lo: the first visible key of each tile's first row (row_keys), or null to read
+// it from position_ids at every step of the search.
+__device__ int kv_block_work(const AttnArgs& f, int b, int bkv, int bq, int n_qtiles, const int* tile_lo) {
   if (!f.causal) return n_qtiles;
   const int k0 = b * bkv;
   const int k_last = min(k0 + bkv, f.Sk) - 1;
@@ -31,7 +55,8 @@ __device__ int kv_block_work(const AttnArgs& f, int b, int bkv, int bq, int n_qt
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     int lo_k, hiex_k;
-    row_keys(f, mid * bq, lo_k, hiex_k);
+    if (tile_lo) lo_k = tile_lo[mid];
+    else row_keys(f, mid * bq, lo_k, hiex_k);
     if (lo_k > k_last) hi = mid; else lo = mid + 1;
   }
   return lo - t0;
@@ -53,6 +78,7 @@ __global__ __launch_bounds__(NT) void schedule_q_kernel(AttnArgs f, int n, int b
                                                         int* __restrict__ q_next) {
   __shared__ int w_s[MAXU];
   __shared__ int start[NB];
+  __shared__ int wsum_s[NWAVE];
   __shared__ int wmax_s;
   const int tid = threadIdx.x;
   if (q_next && tid < 8) q_next[tid] = 0;   // the work queues of the kernel that follows
@@ -77,23 +103,10 @@ __global__ __launch_bounds__(NT) void schedule_q_kernel(AttnArgs f, int n, int b
   auto bucket = [&](int w) { return NB - 1 - (int)(((int64_t)w * (NB - 1)) / wm); };
   for (int u = tid; u < n; u += NT) atomicAdd(&start[bucket(w_s[u])], 1);
   __syncthreads();
-  // exclusive prefix sum of the bucket counts (two buckets per thread, Hillis-Steele
-  // over the per-thread pairs)
+  // exclusive prefix sum of the bucket counts (two buckets per thread)
   static_assert(NB == 2 * NT, "two buckets per thread");
   const int c0 = start[2 * tid], c1 = start[2 * tid + 1];
-  int incl = c0 + c1;
-  __syncthreads();
-  start[2 * tid] = incl;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const int add = tid >= off ? start[2 * (tid - off)] : 0;
-    __syncthreads();
-    incl += add;
-    start[2 * tid] = incl;
-    __syncthreads();
-  }
-  const int excl = incl - c0 - c1;
-  __syncthreads();
+  const int excl = block_incl_scan(c0 + c1, wsum_s) - c0 - c1;
   start[2 * tid] = excl;
   start[2 * tid + 1] = excl + c0;
   __syncthreads();
@@ -114,7 +127,9 @@ __global__ __launch_bounds__(NT) void schedule_kv_xcd_kernel(AttnArgs f, int n, 
                                                              int* __restrict__ next) {
   __shared__ int w_s[MAXU];      // work, then (segment << 27) | work
   __shared__ int start[NB];
-  __shared__ int64_t part[NT];
+  __shared__ int64_t part_w[NWAVE], total_s;
+  __shared__ int wsum_s[NWAVE];
+  __shared__ int tile_lo_s[MAXT];
   __shared__ int wmax_s, seg_start[NXCD + 1];
   const int tid = threadIdx.x;
   if (tid < NXCD) next[tid] = 0;
@@ -126,6 +141,16 @@ __global__ __launch_bounds__(NT) void schedule_kv_xcd_kernel(AttnArgs f, int n, 
   }
   for (int b = tid; b < NB; b += NT) start[b] = 0;
   if (tid == 0) wmax_s = 0;
+  // the first visible key of every query tile, read once (all loads in flight together)
+  // so that the binary searches below run in LDS
+  const bool lds_lo = f.causal && n_qtiles <= MAXT;
+  if (lds_lo) {
+    for (int t = tid; t < n_qtiles; t += NT) {
+      int lo_k, hiex_k;
+      row_keys(f, t * bq, lo_k, hiex_k);
+      tile_lo_s[t] = lo_k;
+    }
+  }
   __syncthreads();
   // work of the blocks; thread t owns the contiguous blocks [t C, t C + C)
   const int C = (n + NT - 1) / NT;
@@ -133,23 +158,18 @@ __global__ __launch_bounds__(NT) void schedule_kv_xcd_kernel(AttnArgs f, int n, 
   int wmax = 0;
   int64_t mine = 0;
   for (int u = u0; u < u1; ++u) {
-    const int w = kv_block_work(f, u, bkv, bq, n_qtiles);
+    const int w = kv_block_work(f, u, bkv, bq, n_qtiles, lds_lo ? tile_lo_s : nullptr);
     w_s[u] = w;
     wmax = max(wmax, w);
     mine += w;
   }
   atomicMax(&wmax_s, wmax);
-  // inclusive scan of the per-thread sums (Hillis-Steele)
-  part[tid] = mine;
+  // inclusive scan of the per-thread sums
+  const int64_t incl_w = block_incl_scan(mine, part_w);
+  if (tid == NT - 1) total_s = incl_w;
   __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const int64_t add = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += add;
-    __syncthreads();
-  }
-  const int64_t total = part[NT - 1];
-  int64_t run = part[tid] - mine;   // work before block u0
+  const int64_t total = total_s;
+  int64_t run = incl_w - mine;   // work before block u0
   for (int u = u0; u < u1; ++u) {
     const int w = w_s[u];
     // segment of the block's midpoint in the cumulative work (by count when there is none)
@@ -170,19 +190,7 @@ __global__ __launch_bounds__(NT) void schedule_kv_xcd_kernel(AttnArgs f, int n, 
   // exclusive prefix sum of the bucket counts (two buckets per thread)
   static_assert(NB == 2 * NT, "two buckets per thread");
   const int c0 = start[2 * tid], c1 = start[2 * tid + 1];
-  int incl = c0 + c1;
-  __syncthreads();
-  start[2 * tid] = incl;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const int add = tid >= off ? start[2 * (tid - off)] : 0;
-    __syncthreads();
-    incl += add;
-    start[2 * tid] = incl;
-    __syncthreads();
-  }
-  const int excl = incl - c0 - c1;
-  __syncthreads();
+  const int excl = block_incl_scan(c0 + c1, wsum_s) - c0 - c1;
   start[2 * tid] = excl;
   start[2 * tid + 1] = excl + c0;
   __syncthreads();
