@@ -5,7 +5,8 @@ their units in natural order.  Checked against the oracle on sampled rows, and a
 every key / row through properties that hold at any size: with all keys visible,
 sum_j dK_j = 0 (the rows of dS sum to zero) and sum_j dV_j = sum_i dO_i summed over
 the query heads of a group (the rows of P sum to one); gradients are written over
-NaN so that a unit that never ran shows."""
+NaN so that a unit that never ran shows.  Also a causal launch past the 8192 query
+tiles whose first visible keys the dK/dV schedule keeps in LDS."""
 
 import numpy as np
 import pytest
@@ -74,3 +75,35 @@ def test_large_grids_sampled_and_sums(usp, Sq, Sk, Hq, Hkv):
     check_lse(lse[:, rd].cpu(), ref_l, "lse")
     rq, _, _ = oracle.attention_bwd(f64(q[rows]), k64, v64, f64(do[rows]), causal=False)
     check_grad(dq[rd].cpu(), rq, "dq")
+
+
+def test_causal_beyond_schedule_tile_table(usp):
+    """Causal packed documents over 8193 query tiles of 64 rows, one more than the dK/dV
+    schedule keeps in LDS for its binary searches (which then read position_ids): one
+    whole document in the middle checked against the oracle run on that document alone
+    (packed documents do not see each other), and every output finite (written over NaN)."""
+    S = 8193 * 64
+    say("causal beyond the schedule's tile table", S)
+    lengths = inputs.doc_lengths(S, 64, 53)
+    q, k, v, do, pos = inputs.attention_case(S, 1, 1, 128, seed=54, lengths=lengths)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    posd = torch.from_numpy(pos).to(DEV)
+    o, lse = usp.blockattn_fwd(qd, kd, vd, posd, causal=True)
+    nan = lambda t: torch.full_like(t, float("nan"))
+    dq, dk, dv = usp.blockattn_bwd(qd, kd, vd, o, lse, dod, posd, causal=True,
+                                   dq=nan(qd), dk=nan(kd), dv=nan(vd))
+    torch.cuda.synchronize()
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t).all()), name
+    starts = np.concatenate([[0], np.cumsum(lengths)])
+    d = len(lengths) // 2
+    a, b = int(starts[d]), int(starts[d + 1])
+    qs, ks, vs, ds = f64(q[a:b]), f64(k[a:b]), f64(v[a:b]), f64(do[a:b])
+    dpos = pos[a:b]   # the document alone: its positions 0 .. L-1
+    ref_o, ref_l = oracle.attention_fwd(qs, ks, vs, pos=dpos, causal=True)
+    check_o(o[a:b].cpu(), ref_o, "o")
+    check_lse(lse[:, a:b].cpu(), ref_l, "lse")
+    rq, rk, rv = oracle.attention_bwd(qs, ks, vs, ds, pos=dpos, causal=True)
+    check_grad(dq[a:b].cpu(), rq, "dq")
+    check_grad(dk[a:b].cpu(), rk, "dk")
+    check_grad(dv[a:b].cpu(), rv, "dv")
