@@ -1,15 +1,20 @@
-"""Oracle: the four-device ring simulation of the Ring Attention glossary page.
+"""Oracle: the four-device ring example of the Ring Attention glossary page.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Ultralytics glossary, "Ring Attention", section "Como funciona la atencion en anillo":
-the sequence is split into N blocks; device i keeps query block i and, at step
-``step``, holds key/value block j = (i - step) mod N.  It accumulates a numerator
-(sum of exp(score) times values) and a denominator (sum of exp(score)) and
-divides them at the end.  The page notes that production kernels also subtract a
-running maximum before exponentiating; ``ring_sim_online`` is that form, carrying
-per row the running max m, the running denominator l and the running numerator.
-Both equal full (non-causal) attention in exact arithmetic.  float64 throughout.
+the sequence is cut into N equal blocks and device i keeps query block i while the
+key/value blocks travel round the ring, so that every device sees every key/value
+block once.  Per query row a device keeps two running sums over the blocks it has
+seen, the exponentiated scores weighted by the values (numerator) and the
+exponentiated scores alone (denominator), and divides one by the other at the end.
+The page adds that production kernels subtract a running maximum before
+exponentiating, for numerical safety.
+
+``ring_sim_raw`` is the first form written as one sum over key blocks (the order in
+which a ring delivers the blocks changes only rounding); ``ring_sim_online`` is the
+running-maximum form, stepping all devices through the ring at once.  Both equal full
+(non-causal) softmax attention in exact arithmetic.  float64 throughout.
 """
 
 import numpy as np
@@ -23,44 +28,43 @@ def full_attention_noncausal(q, k, v):
     return (e / e.sum(axis=1, keepdims=True)) @ v
 
 
+def _blocks(a, n):
+    a = np.asarray(a, dtype=np.float64)
+    if a.shape[0] % n:
+        raise ValueError("the sequence must split into equal blocks")
+    return a.reshape(n, a.shape[0] // n, a.shape[1])
+
+
 def ring_sim_raw(q, k, v, n_devices):
-    """The page's loop: raw exp, numerator/denominator, divide at the end."""
-    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    """Raw exponentials, no maximum: for every query, the per-key-block numerators
+    (exp(scores) @ values) and denominators (sum of exp(scores)) summed over all
+    key blocks, then divided.  q, k, v [S][dim]; returns O [S][dim]."""
+    kb, vb = _blocks(k, n_devices), _blocks(v, n_devices)
+    q = np.asarray(q, dtype=np.float64)
     dim = q.shape[-1]
-    qb, kb, vb = (np.split(a, n_devices) for a in (q, k, v))
-    outs = []
-    for i in range(n_devices):
-        num = np.zeros((qb[i].shape[0], dim))
-        den = np.zeros((qb[i].shape[0], 1))
-        for step in range(n_devices):
-            j = (i - step) % n_devices
-            p = np.exp(qb[i] @ kb[j].T / np.sqrt(dim))
-            num += p @ vb[j]
-            den += p.sum(axis=-1, keepdims=True)
-        outs.append(num / den)
-    return np.concatenate(outs)
+    e = np.exp(np.einsum("sd,jbd->sjb", q, kb) / np.sqrt(dim))   # [query][key block][key]
+    numer = np.einsum("sjb,jbd->sjd", e, vb).sum(axis=1)
+    denom = e.sum(axis=(1, 2))
+    return numer / denom[:, None]
 
 
 def ring_sim_online(q, k, v, n_devices):
-    """Running-max form: per row (m, l, acc); returns (O, LSE) with LSE natural-log."""
-    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
-    dim = q.shape[-1]
-    qb, kb, vb = (np.split(a, n_devices) for a in (q, k, v))
-    outs, lses = [], []
-    for i in range(n_devices):
-        rows = qb[i].shape[0]
-        m = np.full(rows, -np.inf)
-        l = np.zeros(rows)
-        acc = np.zeros((rows, dim))
-        for step in range(n_devices):
-            j = (i - step) % n_devices
-            s = qb[i] @ kb[j].T / np.sqrt(dim)
-            m_new = np.maximum(m, s.max(axis=1))
-            alpha = np.exp(m - m_new)
-            p = np.exp(s - m_new[:, None])
-            l = alpha * l + p.sum(axis=1)
-            acc = alpha[:, None] * acc + p @ vb[j]
-            m = m_new
-        outs.append(acc / l[:, None])
-        lses.append(m + np.log(l))
-    return np.concatenate(outs), np.concatenate(lses)
+    """Running-maximum form.  At ring step t device i holds key/value block
+    (i - t) mod N (the block its predecessor held one step earlier) and updates, per
+    query row, the running max m, the running denominator l and the running
+    numerator; returns (O [S][dim], LSE [S], natural log)."""
+    qb, kb, vb = _blocks(q, n_devices), _blocks(k, n_devices), _blocks(v, n_devices)
+    n, rows, dim = qb.shape
+    m = np.full((n, rows), -np.inf)
+    l = np.zeros((n, rows))
+    numer = np.zeros((n, rows, dim))
+    for t in range(n):
+        kt, vt = np.roll(kb, t, axis=0), np.roll(vb, t, axis=0)   # device i: block (i - t) mod n
+        s = np.einsum("ird,icd->irc", qb, kt) / np.sqrt(dim)
+        m_new = np.maximum(m, s.max(axis=2))
+        alpha = np.exp(m - m_new)
+        p = np.exp(s - m_new[:, :, None])
+        l = alpha * l + p.sum(axis=2)
+        numer = alpha[:, :, None] * numer + np.einsum("irc,icd->ird", p, vt)
+        m = m_new
+    return (numer / l[:, :, None]).reshape(n * rows, dim), (m + np.log(l)).reshape(n * rows)

@@ -48,6 +48,14 @@ def test_ring_example_matches_page():
     assert np.allclose(raw, full, atol=g["allclose_atol"]) == g["matches_full_attention"]
     # in float64 the identity is exact up to rounding
     assert np.max(np.abs(raw - full)) < 1e-12
+    # and both equal the library's softmax attention (torch fp64 SDPA) and the oracle's
+    # forward, so that a mistake shared by the two ring functions cannot pass
+    q64, k64, v64 = (t.numpy().astype(np.float64)[:, None] for t in (q, k, v))
+    ref = _sdpa(q64, k64, v64)[:, 0]
+    o_full, _ = oracle.attention_fwd(q64, k64, v64)
+    assert np.max(np.abs(raw - ref)) < 1e-12
+    assert np.max(np.abs(full - ref)) < 1e-12
+    assert np.max(np.abs(o_full[:, 0] - ref)) < 1e-12
 
 
 def test_ring_online_and_blockwise_equal_full_attention():
@@ -236,11 +244,16 @@ def _loss(q, k, v, do, **kw):
     return float(np.sum(o * do))
 
 
-def test_backward_matches_central_finite_differences():
-    lengths = [5, 7]
-    S = sum(lengths)
+# contiguous packed documents; and one pair of a 3-rank striped layout (local query
+# row a is global token 2 + 3a, local key b is global token 1 + 3b), whose gradient is
+# that of the pair's own attention (normalised over the pair's keys)
+@pytest.mark.parametrize("S, lengths, extra", [
+    (12, [5, 7], {}),
+    (6, [7, 3, 8], dict(q_start=2, q_stride=3, k_start=1, k_stride=3)),
+])
+def test_backward_matches_central_finite_differences(S, lengths, extra):
     pos = _packed_pos(lengths)
-    kw = dict(pos=pos, causal=True, scale=0.7)
+    kw = dict(pos=pos, causal=True, scale=0.7, **extra)
     q, k, v = _rand((S, 2, 4), 40), _rand((S, 1, 4), 41), _rand((S, 1, 4), 42)
     do = _rand((S, 2, 4), 43)
     dq, dk, dv = oracle.attention_bwd(q, k, v, do, threads=1, **kw)
