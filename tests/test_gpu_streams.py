@@ -38,3 +38,31 @@ def test_concurrent_side_streams_match_default(usp):
     for got in (r1, r2):
         for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), got, ref):
             assert torch.equal(a, b), name
+
+
+def test_explicit_stream_argument_matches_default(usp):
+    """Calls given a side stream that is NOT current, with no preallocated outputs or
+    workspace: the binding allocates those while the side stream is current, so work
+    that the current stream enqueues right after the call (here: allocations of the
+    same sizes, filled with NaN) cannot take their memory while the side-stream kernels
+    still use it.  Results equal the default-stream call bit for bit."""
+    say("explicit stream argument")
+    S = 8192
+    q, k, v, do, pos = inputs.attention_case(S, 4, 1, 128, seed=62, lengths=[5000, 3192])
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    posd = torch.from_numpy(pos).to(DEV)
+    ref = _fwd_bwd(usp, qd, kd, vd, dod, posd)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o, lse = usp.blockattn_fwd(qd, kd, vd, posd, stream=side)
+    dq, dk, dv = usp.blockattn_bwd(qd, kd, vd, o, lse, dod, posd, stream=side)
+    # the current stream now allocates and overwrites memory of the sizes the calls
+    # allocated; with the temporaries on the side stream none of it can alias them
+    junk = [torch.full_like(t, float("nan")) for t in (o, lse, dq, dk, dv)]
+    junk += [torch.full((usp.bwd_workspace_bytes(S, S, 4, 1, 128),), 255, dtype=torch.uint8, device=DEV)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), (o, lse, dq, dk, dv), ref):
+        assert torch.equal(a, b), name
+    del junk
