@@ -106,3 +106,39 @@ def ring_256k(with_do=False):
     if with_do:
         return q, k, v, normal(shp, g), position_ids([c["S"]])
     return q, k, v, position_ids([c["S"]])
+
+
+# ---- the benchmark's layer: the packed 128K input as the Ulysses SP=8 layer holds it ----
+
+BENCH_LAYER = dict(P=8, S=131072, Hq=32, Hkv=8, D=128, seed=4, n_docs=16, doc_seed=1)
+
+
+def bench_layer(device):
+    """Sequence-sharded x_q [8][16384][32][128], x_k, x_v [8][16384][8][128] and dO like
+    x_q (bf16 N(0, 1), drawn on `device` with a torch generator seeded 4, in the order
+    x_q, x_k, x_v, dO, float32 then rounded to bf16), the int32 position_ids of the 16
+    packed documents (lengths multinomial over 131072 tokens, numpy seed 1) on `device`,
+    and the lengths.  Rank g's share (heads [4g, 4g + 4) of x_q, head g of x_k, x_v) is
+    the packed long-context workload."""
+    c = BENCH_LAYER
+    lengths = doc_lengths(c["S"], c["n_docs"], c["doc_seed"])
+    g = torch.Generator(device=device)
+    g.manual_seed(c["seed"])
+    P, S_l = c["P"], c["S"] // c["P"]
+
+    def draw(H):
+        return torch.randn((P, S_l, H, c["D"]), generator=g, device=device,
+                           dtype=torch.float32).to(torch.bfloat16)
+
+    xq, xk, xv = draw(c["Hq"]), draw(c["Hkv"]), draw(c["Hkv"])
+    xdo = draw(c["Hq"])
+    pos = torch.from_numpy(position_ids(lengths)).to(device)
+    return xq, xk, xv, xdo, pos, lengths
+
+
+def share_of(x, P, group):
+    """Rank `group`'s head slice of a sequence-sharded [P][S_l][H][D] tensor, in global
+    token order: [P S_l][H/P][D] (plain tensor slicing, no arithmetic)."""
+    Pp, S_l, H, D = x.shape
+    hp = H // P
+    return x[:, :, group * hp:(group + 1) * hp].reshape(Pp * S_l, hp, D)
