@@ -15,7 +15,8 @@
  *     src, dst, o_acc, o_part, lse_acc, lse_part are DEVICE pointers owned by the
  *     caller.  A pointer to an empty tensor (a size of 0) may be NULL.  The
  *     library allocates nothing, frees nothing, keeps no pointer after the call
- *     returns and has no global mutable state.
+ *     returns and has no global mutable state, with one exception:
+ *     blockattn_fwd_noalloc's scratch array (see its declaration).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
  *     work is enqueued on it in stream order; no call synchronises the device.
  *   - Arguments are validated on the host before anything is enqueued: a call
@@ -276,6 +277,30 @@ usp_status usp_striped_attn_bwd(const void* q, const void* k, const void* v, con
                                 const int32_t* position_ids, int32_t causal, float softmax_scale,
                                 usp_dtype in_dtype, void* dq, void* dk, void* dv, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * blockattn_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, outputs, supported dtypes and errors as for blockattn_fwd, without the
+ * workspace: the call uses a library-owned scratch array of USP_NOALLOC_SCRATCH_BYTES
+ * in device memory (one per device, created with the library's code object and held
+ * until the process ends).  It allocates and frees nothing.  When the split-range
+ * partials of a call do not fit the array, the call runs without key-range splits (one
+ * workgroup per query tile and head; same results up to fp32 rounding order, slower for
+ * calls too small to fill the GPU).  A call whose launch order alone does not fit
+ * (Sq above roughly 5e8 rows) returns USP_ERR_WORKSPACE_TOO_SMALL before enqueuing
+ * anything.  USP_ERR_HIP if the scratch array's device address cannot be obtained.
+ * Every call on one device shares that device's array: calls that overlap in time on
+ * one device (on different streams, or from several host threads without ordering)
+ * race and give wrong results; calls in stream order do not.
+ * ------------------------------------------------------------------------- */
+#define USP_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+usp_status blockattn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                 int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D,
+                                 const int32_t* position_ids, int64_t q_start, int64_t k_start,
+                                 int32_t causal, float softmax_scale, usp_dtype in_dtype,
+                                 void* o, usp_dtype o_dtype, float* lse, int64_t lse_ld, void* stream);
 
 #ifdef __cplusplus
 }

@@ -69,6 +69,9 @@ SIGNATURES = {
                                             _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _vp,
                                             _c_int32, _c_float, ctypes.c_int, _vp, _vp, _vp, _vp,
                                             ctypes.c_size_t, _vp]),
+    "blockattn_fwd_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _c_int64, _c_int64, _c_int32, _c_int32,
+                                             _c_int32, _vp, _c_int64, _c_int64, _c_int32, _c_float,
+                                             ctypes.c_int, _vp, ctypes.c_int, _vp, _c_int64, _vp]),
     "usp_ulysses_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, _c_int32, _c_int64, _c_int32, _c_int32,
                                             _c_int32, _c_int32, _vp, _c_int32, _c_float, ctypes.c_int,
                                             _vp, _vp, _c_int64, _vp, ctypes.c_size_t, _vp]),
@@ -360,6 +363,32 @@ def blockattn_fwd(q, k, v, position_ids=None, q_start=0, k_start=0, causal=True,
     return o, lse
 
 
+NOALLOC_SCRATCH_BYTES = 16 << 20    # USP_NOALLOC_SCRATCH_BYTES of include/usp.h
+
+
+def blockattn_fwd_noalloc(q, k, v, o, lse, position_ids=None, q_start=0, k_start=0, causal=True,
+                          scale=None, stream=None, debug=None):
+    """blockattn_fwd for callers that cannot allocate: the library's scratch array is the
+    workspace and the caller passes the outputs o [Sq][Hq][D] (bf16 or float32) and
+    lse [Hq][>= Sq] (float32).  Allocates nothing; returns (o, lse)."""
+    lib = load()
+    Sq, Hq, Sk, Hkv, D = _attn_inputs(q, k, v)
+    if q_start < 0 or k_start < 0:
+        raise ValueError("q_start and k_start must be >= 0")
+    _need(o, "o", shape=(Sq, Hq, D))
+    _dtype_code(o)
+    _need_lse(lse, "lse", Hq, Sq)
+    _check_pos(position_ids, max(q_start + Sq, k_start + Sk), causal, debug)
+    _on_device((("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("position_ids", position_ids)))
+    scale = D ** -0.5 if scale is None else float(scale)
+    _check("blockattn_fwd_noalloc",
+           lib.blockattn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), Sq, Sk, Hq, Hkv, D, _ptr(position_ids),
+                                     q_start, k_start, int(bool(causal)), scale, _dtype_code(q),
+                                     _ptr(o), _dtype_code(o), _ptr(lse), lse.stride(0),
+                                     _stream_handle(stream)))
+    return o, lse
+
+
 def blockattn_bwd(q, k, v, o, lse, dout, position_ids=None, q_start=0, k_start=0, causal=True,
                   scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None, debug=None):
     """Gradients (dq, dk, dv) of blockattn_fwd for upstream gradient dout."""
@@ -614,7 +643,7 @@ def lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
     return o_acc, lse_acc
 
 
-__all__ = ["load", "seq_to_head", "head_to_seq", "blockattn_fwd", "blockattn_bwd",
+__all__ = ["load", "seq_to_head", "head_to_seq", "blockattn_fwd", "blockattn_fwd_noalloc", "blockattn_bwd",
            "ulysses_attn_fwd", "ulysses_attn_bwd", "seq_to_stripe", "stripe_to_seq",
            "striped_attn_fwd", "striped_attn_bwd", "fwd_workspace_bytes", "bwd_workspace_bytes",
            "lse_merge", "position_ids_problem", "debug_enabled", "UspError", "BF16", "F32",

@@ -424,11 +424,12 @@ int fwd_ksplit(int64_t Sq, int64_t Sk, int32_t Hq) {
 // workspace: the query-tile order (sized for the 128-row tiles of the 4-wave
 // variant), the per-XCD work queues, and with a key-range split the partials
 // o_part [Hq][tiles][ksplit][256][128] and lse_part [Hq][tiles][ksplit][256] (fp32)
-size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D, int bf16_path) {
+size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D, int bf16_path,
+                                int allow_split) {
   if (!bf16_path) return 0;
   const size_t n_qtiles = (size_t)((Sq + 127) / 128);
   size_t n = align256(n_qtiles * sizeof(int)) + align256(NXCD * sizeof(int));
-  const int ks = fwd_ksplit(Sq, Sk, Hq);
+  const int ks = allow_split ? fwd_ksplit(Sq, Sk, Hq) : 1;
   if (ks > 1) {
     const size_t slots = (size_t)Hq * (size_t)((Sq + 255) / 256) * ks;
     n += align256(slots * 256 * HD * sizeof(float)) + align256(slots * 256 * sizeof(float));
@@ -436,13 +437,13 @@ size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv,
   return n;
 }
 
-void attn_fwd_workspace_layout(AttnArgs& a, void* base) {
+void attn_fwd_workspace_layout(AttnArgs& a, void* base, int allow_split) {
   char* p = reinterpret_cast<char*>(base);
   a.q_order = reinterpret_cast<int*>(p);
   p += align256((size_t)((a.Sq + 127) / 128) * sizeof(int));
   a.q_next = reinterpret_cast<int*>(p);
   p += align256(NXCD * sizeof(int));
-  a.ksplit = fwd_ksplit(a.Sq, a.Sk, a.Hq);
+  a.ksplit = allow_split ? fwd_ksplit(a.Sq, a.Sk, a.Hq) : 1;
   if (a.ksplit > 1) {
     const size_t slots = (size_t)a.Hq * (size_t)((a.Sq + 255) / 256) * a.ksplit;
     a.o_part = reinterpret_cast<float*>(p);

@@ -139,9 +139,12 @@ __device__ __forceinline__ int first_row_seeing(const AttnArgs& a, int j) {
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int o_f32, hipStream_t s);
 int device_cu_count();
-size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D, int bf16_path);
+// allow_split = 0: the workspace (and layout) of the same call without key-range
+// splits (one workgroup per query tile and head, no partials)
+size_t attn_fwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D, int bf16_path,
+                                int allow_split = 1);
 // fills a.q_order (and the split partials) from the workspace base (bf16 path)
-void attn_fwd_workspace_layout(AttnArgs& a, void* base);
+void attn_fwd_workspace_layout(AttnArgs& a, void* base, int allow_split = 1);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t s);
 
 struct AttnBwdArgs {

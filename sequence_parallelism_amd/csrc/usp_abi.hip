@@ -1,6 +1,7 @@
 // C ABI of the attention share: host-side argument validation and dispatch.
 // Every check runs before anything is enqueued, so a failing call has no effect.
 #include <climits>
+#include <mutex>
 
 #include "common.h"
 
@@ -84,13 +85,14 @@ usp_status attn_fwd_impl(const void* q, const void* k, const void* v, int64_t Sq
                          int32_t Hkv, int32_t D, const int32_t* position_ids, int64_t q_start,
                          int64_t q_stride, int64_t k_start, int64_t k_stride, int32_t causal,
                          float softmax_scale, usp_dtype in_dtype, void* o, usp_dtype o_dtype, float* lse,
-                         int64_t lse_ld, void* workspace, size_t workspace_bytes, void* stream) {
+                         int64_t lse_ld, void* workspace, size_t workspace_bytes, void* stream,
+                         int allow_split = 1) {
   usp_status st = check_attn(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal,
                              in_dtype, o, lse, lse_ld, q_stride, k_stride);
   if (st != USP_OK) return st;
   if (bad_dtype(o_dtype) || (in_dtype == USP_F32 && o_dtype != USP_F32)) return USP_ERR_BAD_DTYPE;
   if (o_dtype == USP_F32 && !aligned(o, 16) && in_dtype == USP_BF16) return USP_ERR_MISALIGNED;
-  const size_t need = attn_fwd_workspace_bytes(Sq, Sk, Hq, Hkv, D, in_dtype == USP_BF16);
+  const size_t need = attn_fwd_workspace_bytes(Sq, Sk, Hq, Hkv, D, in_dtype == USP_BF16, allow_split);
   if (need > 0 && !workspace) return USP_ERR_NULL_POINTER;
   if (workspace && !aligned(workspace, 16)) return USP_ERR_MISALIGNED;
   if (workspace_bytes < need) return USP_ERR_WORKSPACE_TOO_SMALL;
@@ -98,7 +100,7 @@ usp_status attn_fwd_impl(const void* q, const void* k, const void* v, int64_t Sq
                          softmax_scale, o, lse, lse_ld);
   a.q_stride = (int32_t)q_stride;
   a.k_stride = (int32_t)k_stride;
-  if (in_dtype == USP_BF16) attn_fwd_workspace_layout(a, workspace);
+  if (in_dtype == USP_BF16) attn_fwd_workspace_layout(a, workspace, allow_split);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (in_dtype == USP_BF16) return hip_status(launch_attn_fwd_bf16(a, o_dtype == USP_F32, s));
   return hip_status(launch_attn_fwd_f32(a, s));
@@ -364,6 +366,65 @@ usp_status usp_striped_attn_bwd(const void* q, const void* k, const void* v, con
   return attn_bwd_impl(q, k, v, o, lse, lse_ld, dout, S_stripe, S_stripe, Hq, Hkv, D, position_ids, q_rank, P,
                        k_rank, P, causal, softmax_scale, in_dtype, dq, dk, dv, workspace, workspace_bytes,
                        stream);
+}
+
+}  // extern "C"
+
+// ---- blockattn_fwd for callers that cannot allocate ---------------------------------
+//
+// The workspace of blockattn_fwd_noalloc is a file-scope device array (one copy per
+// device, held until the process ends).  Host code never passes the array's name to a
+// kernel or a copy: the name is a host-side stand-in.  The device address of the
+// current device's copy comes from hipGetSymbolAddress, taken once per device on the
+// first call there and kept.
+
+namespace {
+
+constexpr size_t NOALLOC_SCRATCH_BYTES = USP_NOALLOC_SCRATCH_BYTES;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+__device__ __attribute__((aligned(256))) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+std::mutex scratch_mutex;
+void* scratch_ptr[NOALLOC_MAX_DEVICES];
+
+// Device address of the current device's scratch array (NULL on failure).
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+usp_status blockattn_fwd_noalloc(const void* q, const void* k, const void* v, int64_t Sq, int64_t Sk,
+                                 int32_t Hq, int32_t Hkv, int32_t D, const int32_t* position_ids,
+                                 int64_t q_start, int64_t k_start, int32_t causal, float softmax_scale,
+                                 usp_dtype in_dtype, void* o, usp_dtype o_dtype, float* lse, int64_t lse_ld,
+                                 void* stream) {
+  usp_status st = check_attn(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, k_start, causal,
+                             in_dtype, o, lse, lse_ld);
+  if (st != USP_OK) return st;
+  if (bad_dtype(o_dtype) || (in_dtype == USP_F32 && o_dtype != USP_F32)) return USP_ERR_BAD_DTYPE;
+  // the split-range partials when they fit, else the same call without splits
+  const int bf = in_dtype == USP_BF16;
+  int allow_split = 1;
+  if (attn_fwd_workspace_bytes(Sq, Sk, Hq, Hkv, D, bf, 1) > NOALLOC_SCRATCH_BYTES) {
+    allow_split = 0;
+    if (attn_fwd_workspace_bytes(Sq, Sk, Hq, Hkv, D, bf, 0) > NOALLOC_SCRATCH_BYTES)
+      return USP_ERR_WORKSPACE_TOO_SMALL;
+  }
+  void* ws = device_scratch();
+  if (!ws) return USP_ERR_HIP;
+  return attn_fwd_impl(q, k, v, Sq, Sk, Hq, Hkv, D, position_ids, q_start, 1, k_start, 1, causal,
+                       softmax_scale, in_dtype, o, o_dtype, lse, lse_ld, ws, NOALLOC_SCRATCH_BYTES, stream,
+                       allow_split);
 }
 
 }  // extern "C"

@@ -196,3 +196,16 @@ def test_striped_validation(lib):
     assert bwd(qr=-1) == SHAPE
     assert bwd(kr=4) == SHAPE
     assert bwd(dq=None) == NULLP
+
+
+def test_noalloc_rejects_before_touching_the_device(lib):
+    """blockattn_fwd_noalloc validates its arguments, then the size of the workspace the
+    call needs against the library's scratch array, before anything else: a call whose
+    launch order alone exceeds USP_NOALLOC_SCRATCH_BYTES is refused."""
+    def call(q=A, Sq=256, Sk=256, Hq=4, Hkv=1, ld=None):
+        return lib.blockattn_fwd_noalloc(q, A, A, Sq, Sk, Hq, Hkv, 128, A, 0, 0, 1, 0.1, 0, A, 0, A,
+                                         Sq if ld is None else ld, None)
+    assert call(q=None) == NULLP
+    assert call(Hkv=3) == NOTDIV
+    assert call(ld=100) == SHAPE
+    assert call(Sq=600_000_000, Sk=16, Hq=1) == WS      # 4.7M query tiles: 18.75 MB of launch order
