@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the unfused step and the stand-alone permute, merge, ring and "
                          "all-gather measurements (profiling runs)")
+    ap.add_argument("--bandwidth-only", action="store_true",
+                    help="only the stand-alone permute, copy and merge measurements (HBM byte "
+                         "counter runs); prints their JSON line")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain device copy of CALIB_BYTES (calibrates the HBM "
                          "byte counters of a profiling run)")
@@ -116,6 +119,11 @@ def main():
     usp.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.bandwidth_only:
+        g = torch.Generator(device=dev)
+        g.manual_seed(SEED + 100)
+        print(json.dumps({"bandwidth": bandwidth_measurement(torch, usp, dev, g)}), flush=True)
+        return
 
     # ---- inputs, resident in HBM before timing -----------------------------------
     xq, xk, xv, xdo, pos, lengths = inputs.bench_layer(dev)
@@ -324,9 +332,21 @@ def causal_4k_measurement(torch, usp, dev, steps):
 
 
 def extra_measurements(torch, usp, dev, g):
+    """Stand-alone permute, copy and merge bandwidth, the emulated rings and the
+    all-gather comparison."""
+    res = bandwidth_measurement(torch, usp, dev, g)
+    res.update(ring_measurement(torch, usp, dev, g))
+    res.update(striped_measurement(torch, usp, dev, g))
+    res.update(allgather_measurement(torch, usp, dev, g))
+    return res
+
+
+def bandwidth_measurement(torch, usp, dev, g):
     """Stand-alone permute (full bijection of the Ulysses SP=8, 32-head layer) and
     lse_merge (ring blocks of 16384 rows, 2 heads) bandwidth, buffers rotated so
-    that the working set exceeds the 256 MB last-level cache."""
+    that the working set exceeds the 256 MB last-level cache; two copy ceilings of
+    the same bytes: the runtime's device-to-device copy, and the permute kernel
+    itself with one rank (an identity map: a plain contiguous copy)."""
     res = {}
     sets = 3
     xs = [torch.randn((8, 4096, 32, 128), generator=g, device=dev).to(torch.bfloat16)
@@ -368,6 +388,20 @@ def extra_measurements(torch, usp, dev, g):
     copy_gbps = nbytes / (ms / 1e3) / 1e9
     res["hbm_copy_measured_GBps"] = round(copy_gbps, 1)
     res["permute_full_sp8_frac_of_measured_copy"] = round(res["permute_full_sp8_GBps"] / copy_gbps, 4)
+    # the permute kernel with P = 1: [1][32768][32][128] -> the same layout, a contiguous copy
+    flat = lambda t: t.view(1, -1, t.shape[2], t.shape[3])
+    for i in range(sets):
+        usp.seq_to_head(flat(xs[i]), 1, out=flat(zs[i]))
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        usp.seq_to_head(flat(xs[i % sets]), 1, out=flat(zs[i % sets]))
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    kcopy = nbytes / (ms / 1e3) / 1e9
+    res["permute_kernel_as_copy_GBps"] = round(kcopy, 1)
+    res["permute_full_sp8_frac_of_kernel_copy"] = round(res["permute_full_sp8_GBps"] / kcopy, 4)
     del xs, ys, zs
 
     blk, H, nb = 16384, 2, 16
@@ -392,9 +426,6 @@ def extra_measurements(torch, usp, dev, g):
     res["lse_merge_frac_of_hbm_peak"] = round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
     res["lse_merge_us"] = round(ms * 1e3, 2)
     del acc, acc_l, parts, pl
-    res.update(ring_measurement(torch, usp, dev, g))
-    res.update(striped_measurement(torch, usp, dev, g))
-    res.update(allgather_measurement(torch, usp, dev, g))
     return res
 
 

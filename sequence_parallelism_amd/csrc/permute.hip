@@ -45,9 +45,13 @@ __global__ __launch_bounds__(256) void permute_kernel(
     int64_t packed_base_gs0, int64_t packed_g_stride, int64_t packed_s_stride,
     int64_t strided_base_gs0, int64_t strided_g_stride, int64_t strided_s_stride,
     int32_t P, int32_t group, int32_t to_head) {
+  // grid rows run over shards first and head blocks second (gs = s P + g), so the
+  // workgroups resident at one time cover every head block of a few shards: they read
+  // (seq -> head) or write (head -> seq) whole sequence-sharded rows together instead of
+  // one 1/P slice of every row of the tensor
   const uint32_t gs = blockIdx.y;
-  const int32_t g = group >= 0 ? group : (int32_t)(gs / (uint32_t)P);
-  const int32_t s = group >= 0 ? (int32_t)gs : (int32_t)(gs % (uint32_t)P);
+  const int32_t g = group >= 0 ? group : (int32_t)(gs % (uint32_t)P);
+  const int32_t s = group >= 0 ? (int32_t)gs : (int32_t)(gs / (uint32_t)P);
   const int64_t packed_off = packed_base_gs0 + g * packed_g_stride + s * packed_s_stride;
   const int64_t strided_off = strided_base_gs0 + g * strided_g_stride + s * strided_s_stride;
   const uint32_t run_vec = per_run.d;
