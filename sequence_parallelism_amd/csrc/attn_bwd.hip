@@ -58,15 +58,10 @@ __host__ __device__ constexpr int sdp_order(int j) {
 static_assert(sdp_order(4) == 8 && sdp_order(5) == 4 && sdp_order(11) == 7 && sdp_order(10) == 11 &&
               sdp_order(12) == 12 && sdp_order(15) == 15, "S / dP order");
 
-// acc += A B with the accumulator pinned to AGPRs (the dK^T, dV^T accumulators stay
-// there for the whole kernel, leaving the VGPRs to everything else).  Issued as
-// inline assembly, so the compiler inserts no MFMA wait states around it: the
-// operands' producers are far ahead (B by at least eight MFMA steps, A by a waited
-// LDS read), the s_nop covers a VALU write right before, and the accumulators are
-// read only after the padding that follows the item loops.
-__device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
+// The dK^T, dV^T accumulators stay in AGPRs for the whole kernel (mfma32_acc), leaving
+// the VGPRs to everything else; the operands' producers are far ahead (B by at least
+// eight MFMA steps, A by a waited LDS read), and the accumulators are read only after
+// the padding that follows the item loops.
 
 // ---- 2. main ----------------------------------------------------------------------
 // One work unit: unit x + NXCD k belongs to XCD x; with m = Hkv nch units per key
@@ -220,13 +215,16 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
     return r;
   };
 
-  // DMA j (0..7) of an item into buffer buf: load i = j/2 of tile u = j%2.  vq carries
-  // the clamped row offset from tile 0 to tile 1 of the same load.
-  auto dma_step = [&](int j, const ItemSrc& src, int buf, uint32_t& vq) {
-    const int i = j >> 1, u = j & 1;
-    const uint32_t lds = stage_lds + (uint32_t)(((buf * 2 + u) * TILE + (4 * i + wave) * 512) * 2);
+  // DMA j (0..7) of an item into the buffer whose base (for this wave) is `base`: load
+  // i = j/2 of tile u = j%2, at a constant offset from the base.  vq carries the clamped
+  // row offset from tile 0 to tile 1 of the same load.
+  auto dma_base = [&](int buf) {
+    return __builtin_amdgcn_readfirstlane(stage_lds + (uint32_t)((buf * 2 * TILE + wave * 512) * 2));
+  };
+  auto dma_step = [&](auto J, const ItemSrc& src, uint32_t base, uint32_t& vq) {
+    constexpr int j = decltype(J)::v, i = j >> 1, u = j & 1;
     if (u == 0) vq = min(rq_row + 16 * i, src.lim) * rowqB + rq_lc;
-    dma16(src.tile[u], vq, __builtin_amdgcn_readfirstlane(lds));
+    dma16_at<(uint32_t)((u * TILE + 4 * i * 512) * 2)>(src.tile[u], vq, base);
   };
 
   // Row scalars of an item (written by the dQ kernel), one row per lane, read one item
@@ -287,7 +285,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
     constexpr int qb = decltype(QB)::v, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
     e4[qb][g4] = *reinterpret_cast<const f32x4*>(&scal_s[1][b][q + 4 * hi]);
   };
-  bf16x8 ops[PF];   // operand reads in flight, carried from item to item
+  bf16x8 ops[2 * PF];   // operand reads in flight (a ring of 2 PF), carried from item to item
 
   // item 0 is staged before the loop; nx: where item it+1 comes from (used by item
   // it), worked out during item it-1; (h2, t2): item it+2 (the last item repeats
@@ -312,7 +310,8 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
   if (it1 - it0 > 2) next_item(h2, t2);
   if (it0 < it1) {
     uint32_t vq = 0;
-    for (int j = 0; j < 8; ++j) dma_step(j, src0, 0, vq);
+    const uint32_t base0 = dma_base(0);
+    unroll<8>([&](auto J) { dma_step(J, src0, base0, vq); });
     load_scalars(src0);
     wait_vmem();
     store_scalars(0);
@@ -334,6 +333,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
       f32x4 l4[2][4];
       bf16x8 pb[2][2], sb[2][2];
       uint32_t vq = 0;
+      const uint32_t dbase = dma_base(buf ^ 1);   // item it+1 goes to the other buffer
 
       // P and dS of element e of 32-row block qb (row 32qb + 8(e/4) + 4hi + e%4), in two
       // stages one step apart so that no instruction waits on the exponential:
@@ -372,7 +372,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
           }
         }
       };
-      mfma_pipeline_carry<PF, 64>(
+      mfma_pipeline_carry2<PF, 64>(
           ops,
           [&](auto I) {   // LDS operand of MFMA i; past the item, the next item's first ones
             constexpr int i = decltype(I)::v;
@@ -412,7 +412,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
               load_rows(IC<qb>{}, IC<g4>{});
             }
             if constexpr (i >= 8 && i < 12) load_nd(IC<1>{}, IC<i - 8>{}, buf);
-            if constexpr (i % 4 == 1 && i < 32) dma_step(i / 4, nx, buf ^ 1, vq);   // item it+1
+            if constexpr (i % 4 == 1 && i < 32) dma_step(IC<i / 4>{}, nx, dbase, vq);   // item it+1
             if constexpr (i == 2) load_scalars(nx);                               // its row scalars
             if constexpr (i == 50) {
               // where item it+2 is (item it's last use of nx, its DMA, is behind it), and
@@ -457,7 +457,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
 #pragma unroll 1
   for (int it = max(it0, n_full); it < it1; ++it) run_item(IC<1>{}, it);
   // the last accumulations (inline-assembly MFMAs) complete before any read below
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  agpr_acc_fence();
   // ---- dK = scale dK^T, dV = dV^T (bf16), lane: key kl, d = 32db + 8g4 + 4hi + 0..3
   if (SPLIT) {   // the chunk's partial sums, unscaled
     if (key_ok) {

@@ -14,6 +14,21 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// acc += A B with the accumulator pinned to AGPRs for the whole kernel (the register
+// allocator can then neither copy it nor give it a second home across branches), issued
+// as inline assembly, so the compiler inserts no MFMA wait states around it.  The caller
+// guarantees the hazards away: a and b were written by VALU instructions at least two
+// instructions earlier (or come from a waited LDS read), and every non-MFMA read of the
+// accumulator is preceded by padding (agpr_acc_fence).
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Padding after the last mfma32_acc before its accumulators are read by other
+// instructions (the accumulation has completed by then).
+__device__ __forceinline__ void agpr_acc_fence() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
 // LDS tiles (rows of 128 bf16 = 16 chunks of 16 bytes) are unpadded; chunk c of row r
 // is stored at c ^ swz16(r).  With it, 16 lanes reading 16 consecutive rows at one
 // logical chunk touch all 64 banks once.
@@ -65,6 +80,29 @@ __device__ __forceinline__ void mfma_pipeline_carry(bf16x8 (&ops)[PF], Load&& lo
   });
 }
 
+// The carried pipeline with the reads issued in pairs, each pair in reverse order of use:
+// at even step i the reads for MFMAs i+PF+1 and then i+PF.  LDS reads complete in
+// order, so the wait for MFMA i+PF's operand also covers MFMA i+PF+1's, and the
+// compiler emits one wait per two MFMAs.  The ring has 2 PF slots; on entry it holds the
+// reads for MFMAs 0 .. PF-1 (slots 0 .. PF-1), on exit those of the next call (NS must be
+// a multiple of 2 PF).
+template <int PF, int NS, typename Load, typename Mma, typename Side>
+__device__ __forceinline__ void mfma_pipeline_carry2(bf16x8 (&ops)[2 * PF], Load&& load, Mma&& mma, Side&& side) {
+  constexpr int R = 2 * PF;
+  static_assert(NS % R == 0, "the ring must line up with the next call");
+  unroll<NS>([&](auto I) {
+    constexpr int i = decltype(I)::v;
+    const bf16x8 op = ops[i % R];
+    if constexpr (i % 2 == 0) {
+      ops[(i + PF + 1) % R] = load(IC<i + PF + 1>{});
+      ops[(i + PF) % R] = load(IC<i + PF>{});
+    }
+    mma(I, op);
+    side(I);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
 // LDS-DMA of 16 bytes per lane from sbase + voff (sbase wave-uniform): lane l's data
 // lands at LDS byte address lds + 16 l.  Issued as inline assembly so that the
 // compiler does not guard every later LDS read with a wait for it; completion is
@@ -72,6 +110,13 @@ __device__ __forceinline__ void mfma_pipeline_carry(bf16x8 (&ops)[PF], Load&& lo
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+}
+// The same with the LDS address lds_base + OFF (OFF a compile-time constant): one scalar
+// add sets M0.
+template <uint32_t OFF>
+__device__ __forceinline__ void dma16_at(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_base), "i"(OFF) : "memory");
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
