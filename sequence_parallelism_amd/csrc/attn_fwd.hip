@@ -10,7 +10,7 @@
 // bf16 / head dim 128 kernel (MFMA):
 //   * a workgroup is 8 wavefronts (2 per SIMD) and owns 256 query rows of one head;
 //     each wave owns 32 rows and keeps its Q fragment in registers;
-//   * key tiles of 64 keys are staged in double-buffered LDS, K and V row-major; the
+//   * key tiles of 128 keys are staged in double-buffered LDS, K and V row-major; the
 //     S^T operands are 16-byte reads of K, the O^T operands (V transposed) two
 //     8-byte transposing reads of V (ds_read_b64_tr_b16).  The next tile comes by
 //     LDS-DMA, issued behind the current tile's score MFMAs, so one barrier per
@@ -42,10 +42,11 @@ namespace {
 using namespace gfx950;
 
 constexpr int HD = 128;          // head dim of the MFMA path
-constexpr int BC = 64;           // keys per LDS tile
+constexpr int BC = 128;          // keys per LDS tile
 constexpr int PF = 4;            // LDS operand reads in flight ahead of their MFMA
 constexpr float RESCALE_TH = 8.f;  // log2 of the largest P allowed before the max moves
-constexpr int TILE = BC * HD;    // elements of one staged tile (16 KB)
+constexpr int TILE = BC * HD;    // elements of one staged tile (32 KB)
+constexpr int NKB = BC / 32;     // 32-key blocks per tile
 constexpr int NXCD = 8;          // MI355X dispatches workgroup i to XCD i % 8
 
 // NW wavefronts (32 query rows each) per workgroup: 8 normally (one workgroup per
@@ -92,7 +93,7 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
   for (int w = 1; w < NW; ++w) { g_lo = min(g_lo, red[w][0]); g_hiex = max(g_hiex, red[w][1]); }
   g_lo = __builtin_amdgcn_readfirstlane(g_lo);
   g_hiex = __builtin_amdgcn_readfirstlane(g_hiex);
-  // local key range [kb, ke); tiles start on 64-key boundaries (inside one block of
+  // local key range [kb, ke); tiles start on 128-key boundaries (inside one block of
   // the key layout, and on the 16-key groups of the V^T slot order)
   int ke = g_hiex;
   int kb = g_lo & ~(BC - 1);
@@ -177,21 +178,21 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
     const bf16* Kb = &stage[buf][0];
     const bf16* Vb = &stage[buf][TILE];
     const int ktn = min(kt + BC, last_kt);   // the last tile fetches itself again (unused)
-    // ---- S^T tile: 64 keys x 32 queries (MFMA i: key block i%2, d chunk i/2); the
+    // ---- S^T tile: 128 keys x 32 queries (MFMA i: 32-key block i%4, d chunk i/4); the
     // next tile's DMA rides along --------------------------------------------------
-    f32x16 sacc[2];
-    mfma_pipeline<PF, 16>(
+    f32x16 sacc[NKB];
+    mfma_pipeline<PF, 8 * NKB>(
         [&](auto I) {
           constexpr int i = decltype(I)::v;
-          return *reinterpret_cast<const bf16x8*>(&Kb[32 * (i & 1) * HD + (kbase ^ (16 * (i >> 1)))]);
+          return *reinterpret_cast<const bf16x8*>(&Kb[32 * (i % NKB) * HD + (kbase ^ (16 * (i / NKB)))]);
         },
         [&](auto I, const bf16x8& op) {
           constexpr int i = decltype(I)::v;
-          sacc[i & 1] = mfma32(op, qf[i >> 1], i < 2 ? f32x16{} : sacc[i & 1]);
+          sacc[i % NKB] = mfma32(op, qf[i / NKB], i < NKB ? f32x16{} : sacc[i % NKB]);
         },
         [&](auto I) {
           constexpr int i = decltype(I)::v;
-          constexpr int every = 16 / (2 * NL);   // the 2 NL loads spread over 16 MFMAs
+          constexpr int every = 8 * NKB / (2 * NL);   // the 2 NL loads spread over the S MFMAs
           if constexpr (i % every == 1 % every) dma_step(i / every, ktn, buf ^ 1);
         });
     // ---- mask, row max ------------------------------------------------------------
@@ -202,7 +203,7 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
       const int lo_k = klo - kt - 4 * hi;
       const int hi_k = khi - 1 - kt - 4 * hi;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < NKB; ++kb2) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int c = 32 * kb2 + 8 * (i >> 2) + (i & 3);
@@ -212,7 +213,7 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
     }
     float mloc = -INFINITY;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int kb2 = 0; kb2 < NKB; ++kb2) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[kb2][i]);
     }
@@ -229,10 +230,10 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     // ---- P = 2^(s*sl2 - m), row sum, bf16 B operands ------------------------------
-    bf16x8 pb[4];
+    bf16x8 pb[2 * NKB];
     float psum = 0.f;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int kb2 = 0; kb2 < NKB; ++kb2) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -245,7 +246,7 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
     }
     l_run += psum;
     // ---- O^T += V^T P^T (MFMA i: key chunk c = i/4, head-dim block db = i%4) --------
-    mfma_pipeline<PF, 16>(
+    mfma_pipeline<PF, 8 * NKB>(
         [&](auto I) {
           constexpr int i = decltype(I)::v;
           const char* t = reinterpret_cast<const char*>(Vb) + 16 * (i >> 2) * HD * 2;
@@ -299,7 +300,7 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
 // so that a faster XCD finishes a slower one's work.
 template <bool O_F32, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int n_qtiles, int n_units) {
-  // per buffer: K [64 keys][128], V [64 keys][128] (swz16)
+  // per buffer: K [128 keys][128], V [128 keys][128] (swz16)
   __shared__ __attribute__((aligned(16))) bf16 stage[2][2 * TILE];
   __shared__ int red[NW][2];
   __shared__ int unit_s;
