@@ -11,21 +11,24 @@
 //                 scalars of the dK/dV kernel (lse log2 e, -D, the visible keys);
 //   2. dK, dV:    a workgroup owns 128 keys of one key/value head (32 per wave; K
 //                 and V of the lane's key are B operands in registers) and walks the
-//                 64-row query tiles that can see the block, for every query head of
+//                 128-row query tiles that can see the block, for every query head of
 //                 the group (one "item" = one (head, tile) pair).  An item is Q and
-//                 dO row-major (32 KB), brought into double-buffered LDS by LDS-DMA
+//                 dO row-major (64 KB), brought into double-buffered LDS by LDS-DMA
 //                 one item ahead; the operands of dV^T and dK^T, which need Q and dO
 //                 transposed, are read from the same tiles with the transposing LDS
 //                 read (two 8-byte reads per operand cost about as much as one
 //                 16-byte read).  Per item each wave
-//                 runs one software pipeline of 64 MFMAs (v_mfma_f32_32x32x16_bf16,
-//                 one key per lane, 16 rows per lane):
-//                   S, dP of rows 0-31 | S, dP of rows 32-63 | dV^T, dK^T of rows
-//                   0-31 | dV^T, dK^T of rows 32-63,
+//                 runs one software pipeline of 128 MFMAs (v_mfma_f32_32x32x16_bf16,
+//                 one key per lane, 16 rows per lane) in eight slots of 16, for the
+//                 four 32-row blocks b:
+//                   S, dP of b0 | S, dP of b1 | dV^T, dK^T of b0 | S, dP of b2 |
+//                   dV^T, dK^T of b1 | S, dP of b3 | dV^T, dK^T of b2 | dV^T, dK^T of b3,
 //                 and after every MFMA it issues one piece of independent work that
 //                 the matrix core's execution hides: the next item's DMA (spread over
-//                 the whole item), and P and dS of the previous 32 rows (exp2,
-//                 products, bf16 packing).
+//                 the first half of the item), and P and dS of the block whose S and
+//                 dP the previous slot finished (exp2, products, bf16 packing).  The
+//                 per-item bookkeeping (the next items' addresses, the publishing
+//                 barrier, the row scalars) is paid once per 128 MFMAs.
 // Query tiles that cannot see the key block are not visited (the first visible
 // tile follows from the block's first key, the last from a binary search over
 // document starts).  Fully visible tiles run first, without any masking work; the
@@ -42,12 +45,23 @@ using namespace gfx950;
 constexpr int HD = 128;
 constexpr int NWB = 4;              // wavefronts per workgroup
 constexpr int BKV = 32 * NWB;       // keys per workgroup
-constexpr int BQ = 64;              // query rows per item
+constexpr int BQ = 128;             // query rows per item
+constexpr int NQB = BQ / 32;        // 32-row blocks per item
 constexpr int PF = 4;               // LDS operand reads in flight ahead of their MFMA
 constexpr int NXCD = 8;             // MI355X dispatches workgroup i to XCD i % 8
-constexpr int TILE = BQ * HD;       // elements of one staged tile (16 KB)
-static_assert(TILE / 8 == 4 * NWB * 64, "a staged tile is four 64-lane DMA loads per wave");
-static_assert(BQ == 64, "one lane per query row stages the row scalars");
+constexpr int TILE = BQ * HD;       // elements of one staged tile (32 KB)
+constexpr int NLQ = TILE / 8 / (NWB * 64);   // 64-lane DMA loads per wave per staged tile
+static_assert(NLQ == 8, "a staged tile is eight 64-lane DMA loads per wave");
+static_assert(BQ == 128, "each lane stages the row scalars of two query rows");
+
+// The 8 slots of 16 MFMAs of an item: S and dP of a 32-row block ("S", sdp_order) or
+// its dV^T and dK^T ("K"), in the order S0 S1 K0 S2 K1 S3 K2 K3, so that block b's
+// softmax runs beside the slot after its S (sm_slot) and at most two blocks' S, dP
+// accumulators and P, dS operands are alive at once (block b uses set b % 2).
+__host__ __device__ constexpr bool slot_is_s(int s) { return s == 0 || s == 1 || s == 3 || s == 5; }
+__host__ __device__ constexpr int slot_blk(int s) { return s < 2 ? s : s == 2 ? 0 : s == 3 ? 2 : s == 4 ? 1 : s == 5 ? 3 : s - 4; }
+__host__ __device__ constexpr int sm_slot(int b) { return b == 0 ? 1 : b == 1 ? 2 : b == 2 ? 4 : 6; }
+static_assert(slot_blk(6) == 2 && slot_blk(7) == 3 && !slot_is_s(7) && slot_is_s(5), "slot order");
 
 // Order of the 16 S / dP MFMAs of a 32-row block (value 8 dp + kk): four S steps
 // first, so that -D (the dP accumulator's start) has arrived from LDS by the first
@@ -70,8 +84,8 @@ static_assert(sdp_order(4) == 8 && sdp_order(5) == 4 && sdp_order(11) == 7 && sd
 // range of equal work, heaviest first; -1 pads a short list).  SPLIT: the unit is
 // chunk c of its key block's items (a.kv_split chunks) and writes its partial dK^T,
 // dV^T sums for the combine pass.
-typedef bf16 StageBuf[2][2 * 64 * 128];   // per buffer: Q [64 rows][128], dO [64][128] (swz16)
-typedef uint32_t ScalBuf[4][2][64];       // per buffer: lse log2(e), -D, klo, khi per row
+typedef bf16 StageBuf[2][2 * BQ * HD];   // per buffer: Q [128 rows][128], dO [128][128] (swz16)
+typedef uint32_t ScalBuf[4][2][BQ];      // per buffer: lse log2(e), -D, klo, khi per row
 template <bool SPLIT>
 __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles, int unit, StageBuf& stage,
                                               ScalBuf& scal_s) {
@@ -179,7 +193,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
   const int it1 = SPLIT ? (int)((int64_t)(chunk + 1) * n_items / nch) : n_items;
 
   // ---- staging of one item by LDS-DMA ------------------------------------------------
-  // Tile u (Q, dO) is 1024 16-byte chunks; wave w, load i covers physical chunks
+  // Tile u (Q, dO) is 2048 16-byte chunks; wave w, load i (0..7) covers physical chunks
   // [(4i + w) * 64, +64), lane l the chunk (4i + w) * 64 + l, i.e. row 16i + 4w + l/16,
   // physical chunk l%16.  Load i's rows are load 0's plus 16i; the swizzle depends on
   // the row modulo 16 only, so one lane offset suffices.
@@ -215,7 +229,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
     return r;
   };
 
-  // DMA j (0..7) of an item into the buffer whose base (for this wave) is `base`: load
+  // DMA j (0..15) of an item into the buffer whose base (for this wave) is `base`: load
   // i = j/2 of tile u = j%2, at a constant offset from the base.  vq carries the clamped
   // row offset from tile 0 to tile 1 of the same load.
   auto dma_base = [&](int buf) {
@@ -231,13 +245,14 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
   // ahead: wave w loads plane w, with no arithmetic on the value (that would stall the
   // pipeline it sits in for a whole memory latency), and stores it at the item's
   // publishing barrier.
-  uint32_t p_sc = 0;
-  auto load_scalars = [&](const ItemSrc& src) { p_sc = src.sc[lane]; };
+  uint32_t p_sc[2] = {0, 0};
+  auto load_scalars = [&](const ItemSrc& src) { p_sc[0] = src.sc[lane]; p_sc[1] = src.sc[lane + 64]; };
   auto store_scalars = [&](int buf) {
     // consumed here, so that no load is left in flight on any path (the compiler
     // would otherwise wait for all memory traffic before reusing the register)
-    asm volatile("" :: "v"(p_sc));
-    scal_s[wave][buf][lane] = p_sc;
+    asm volatile("" :: "v"(p_sc[0]), "v"(p_sc[1]));
+    scal_s[wave][buf][lane] = p_sc[0];
+    scal_s[wave][buf][lane + 64] = p_sc[1];
   };
 
   // items run over the fully visible tiles (each tile for every head of the group in
@@ -268,13 +283,13 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
 
   // LDS operand of MFMA i of the item staged in buffer b
   auto op_at = [&](auto I, int b) {
-    constexpr int i = decltype(I)::v, slot = i / 16, j = i % 16;
-    if constexpr (slot < 2) {   // S or dP of block qb = slot, k-step kk (sdp_order)
+    constexpr int i = decltype(I)::v, slot = i / 16, j = i % 16, qb = slot_blk(slot);
+    if constexpr (slot_is_s(slot)) {   // S or dP of block qb, k-step kk (sdp_order)
       constexpr int dp = sdp_order(j) >> 3, kk = sdp_order(j) & 7;
       const bf16* t = &stage[b][(dp ? 1 : 0) * TILE];
-      return *reinterpret_cast<const bf16x8*>(&t[32 * slot * HD + (qbase ^ (16 * kk))]);
+      return *reinterpret_cast<const bf16x8*>(&t[32 * qb * HD + (qbase ^ (16 * kk))]);
     } else {                    // dV^T (even: dO) / dK^T (odd: Q), row chunk c, head-dim block db
-      constexpr int c = 2 * (slot - 2) + (j >> 3), db = (j >> 1) & 3;
+      constexpr int c = 2 * qb + (j >> 3), db = (j >> 1) & 3;
       const char* t = reinterpret_cast<const char*>(&stage[b][((j & 1) ? 0 : 1) * TILE]) + 16 * c * HD * 2;
       return read_tr_pair(t + tr_off[db][0], t + tr_off[db][1]);
     }
@@ -283,7 +298,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
   f32x4 e4[2][4];
   auto load_nd = [&](auto QB, auto G4, int b) {
     constexpr int qb = decltype(QB)::v, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
-    e4[qb][g4] = *reinterpret_cast<const f32x4*>(&scal_s[1][b][q + 4 * hi]);
+    e4[qb % 2][g4] = *reinterpret_cast<const f32x4*>(&scal_s[1][b][q + 4 * hi]);
   };
   bf16x8 ops[2 * PF];   // operand reads in flight (a ring of 2 PF), carried from item to item
 
@@ -311,7 +326,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
   if (it0 < it1) {
     uint32_t vq = 0;
     const uint32_t base0 = dma_base(0);
-    unroll<8>([&](auto J) { dma_step(J, src0, base0, vq); });
+    unroll<2 * NLQ>([&](auto J) { dma_step(J, src0, base0, vq); });
     load_scalars(src0);
     wait_vmem();
     store_scalars(0);
@@ -341,25 +356,25 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
       float pv[2][16];
       float ds_prev = 0.f;
       auto soft_a = [&](auto QB, auto E) {
-        constexpr int qb = decltype(QB)::v, e = decltype(E)::v;
-        pv[qb][e] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][e], sl2, -l4[qb][e >> 2][e & 3]));
+        constexpr int x = decltype(QB)::v % 2, e = decltype(E)::v;
+        pv[x][e] = __builtin_amdgcn_exp2f(fmaf(sacc[x][e], sl2, -l4[x][e >> 2][e & 3]));
       };
       auto soft_b = [&](auto QB, auto E) {
-        constexpr int qb = decltype(QB)::v, e = decltype(E)::v;
-        const float ds = pv[qb][e] * dpacc[qb][e];   // dP - D (the accumulator started at -D)
+        constexpr int x = decltype(QB)::v % 2, e = decltype(E)::v;
+        const float ds = pv[x][e] * dpacc[x][e];   // dP - D (the accumulator started at -D)
         if constexpr (e & 1) {
-          pb[qb][e >> 3][(e & 7) - 1] = (bf16)pv[qb][e - 1];
-          pb[qb][e >> 3][e & 7] = (bf16)pv[qb][e];
-          sb[qb][e >> 3][(e & 7) - 1] = (bf16)ds_prev;
-          sb[qb][e >> 3][e & 7] = (bf16)ds;
+          pb[x][e >> 3][(e & 7) - 1] = (bf16)pv[x][e - 1];
+          pb[x][e >> 3][e & 7] = (bf16)pv[x][e];
+          sb[x][e >> 3][(e & 7) - 1] = (bf16)ds_prev;
+          sb[x][e >> 3][e & 7] = (bf16)ds;
         } else {
           ds_prev = ds;
         }
       };
       // row scalars of rows 32qb + 8g4 + 4hi + 0..3, read four steps before first use
       auto load_rows = [&](auto QB, auto G4) {
-        constexpr int qb = decltype(QB)::v, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
-        l4[qb][g4] = *reinterpret_cast<const f32x4*>(&scal_s[0][buf][q + 4 * hi]);
+        constexpr int qb = decltype(QB)::v, x = qb % 2, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
+        l4[x][g4] = *reinterpret_cast<const f32x4*>(&scal_s[0][buf][q + 4 * hi]);
         if constexpr (MASK) {
           const int4 lov = *reinterpret_cast<const int4*>(&scal_s[2][buf][q + 4 * hi]);
           const int4 hiv = *reinterpret_cast<const int4*>(&scal_s[3][buf][q + 4 * hi]);
@@ -368,53 +383,57 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const bool vis = (kl >= loa[e]) & (kl < hia[e]) & key_ok;
-            l4[qb][g4][e] = vis ? l4[qb][g4][e] : INFINITY;
+            l4[x][g4][e] = vis ? l4[x][g4][e] : INFINITY;
           }
         }
       };
-      mfma_pipeline_carry2<PF, 64>(
+      mfma_pipeline_carry2<PF, 16 * 2 * NQB>(
           ops,
           [&](auto I) {   // LDS operand of MFMA i; past the item, the next item's first ones
             constexpr int i = decltype(I)::v;
-            if constexpr (i < 64) return op_at(I, buf);
-            else return op_at(IC<i - 64>{}, buf ^ 1);
+            if constexpr (i < 32 * NQB) return op_at(I, buf);
+            else return op_at(IC<i - 32 * NQB>{}, buf ^ 1);
           },
           [&](auto I, const bf16x8& op) {
-            constexpr int i = decltype(I)::v, slot = i / 16, j = i % 16;
-            if constexpr (slot < 2) {
+            constexpr int i = decltype(I)::v, slot = i / 16, j = i % 16, qb = slot_blk(slot), x = qb % 2;
+            if constexpr (slot_is_s(slot)) {
               constexpr int dp = sdp_order(j) >> 3, kk = sdp_order(j) & 7;
               if constexpr (dp) {
                 if constexpr (kk == 0) {   // dP starts from -D of the element's row
                   f32x16 c;
 #pragma unroll
-                  for (int e = 0; e < 16; ++e) c[e] = e4[slot][e >> 2][e & 3];
-                  dpacc[slot] = mfma32(op, vf[0], c);
+                  for (int e = 0; e < 16; ++e) c[e] = e4[x][e >> 2][e & 3];
+                  dpacc[x] = mfma32(op, vf[0], c);
                 } else {
-                  dpacc[slot] = mfma32(op, vf[kk], dpacc[slot]);
+                  dpacc[x] = mfma32(op, vf[kk], dpacc[x]);
                 }
               } else {
-                sacc[slot] = mfma32(op, kf[kk], kk == 0 ? f32x16{} : sacc[slot]);
+                sacc[x] = mfma32(op, kf[kk], kk == 0 ? f32x16{} : sacc[x]);
               }
             } else {
               // k-slot s of lane half hi in row chunk c is row 16c + 8(s/4) + 4hi + s%4,
               // which matches P / dS element 8(c%2) + s of block c/2
-              constexpr int qb = slot - 2, cc = j >> 3, db = (j >> 1) & 3;
-              if constexpr (j & 1) mfma32_acc(dka[db], op, sb[qb][cc]);
-              else mfma32_acc(dva[db], op, pb[qb][cc]);
+              constexpr int cc = j >> 3, db = (j >> 1) & 3;
+              if constexpr (j & 1) mfma32_acc(dka[db], op, sb[x][cc]);
+              else mfma32_acc(dva[db], op, pb[x][cc]);
             }
           },
           [&](auto I) {   // work hidden behind MFMA i
             constexpr int i = decltype(I)::v, slot = i / 16, j = i % 16;
-            // block qb's softmax runs in slot qb + 1; rows of group g4 are read at
-            // step 16 qb + 12 + 4 g4
-            if constexpr (i >= 12 && i <= 40 && i % 4 == 0) {
-              constexpr int qb = i < 28 ? 0 : 1, g4 = (i - 12 - 16 * qb) / 4;
-              load_rows(IC<qb>{}, IC<g4>{});
-            }
+            // block b's softmax runs in slot sm_slot(b); its rows of group g4 are read four
+            // steps before their first use
+            unroll<NQB>([&](auto B) {
+              constexpr int qb = decltype(B)::v, s0 = 16 * sm_slot(qb);
+              if constexpr (i >= s0 - 4 && i <= s0 + 8 && (i - s0) % 4 == 0)
+                load_rows(IC<qb>{}, IC<(i - s0 + 4) / 4>{});
+            });
+            // -D of block b before its S slot, after block b-2 has used the same registers
             if constexpr (i >= 8 && i < 12) load_nd(IC<1>{}, IC<i - 8>{}, buf);
-            if constexpr (i % 4 == 1 && i < 32) dma_step(IC<i / 4>{}, nx, dbase, vq);   // item it+1
-            if constexpr (i == 2) load_scalars(nx);                               // its row scalars
-            if constexpr (i == 50) {
+            if constexpr (i >= 41 && i < 45) load_nd(IC<2>{}, IC<i - 41>{}, buf);
+            if constexpr (i >= 73 && i < 77) load_nd(IC<3>{}, IC<i - 73>{}, buf);
+            if constexpr (i % 4 == 1 && i < 8 * NLQ) dma_step(IC<i / 4>{}, nx, dbase, vq);   // item it+1
+            if constexpr (i == 2) load_scalars(nx);                                   // its row scalars
+            if constexpr (i == 108) {
               // where item it+2 is (item it's last use of nx, its DMA, is behind it), and
               // the step to item it+3; pinned here so that the compiler does not sink this
               // scalar work to the end of the item, where no MFMA runs beside it
@@ -427,7 +446,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
               t2 = adv ? tn : t2;
               asm volatile("" :: "s"(h2), "s"(t2));
             }
-            if constexpr (i == 56) {
+            if constexpr (i == 120) {
               // item it+1 has landed (its DMA was issued in the first half of this item),
               // and so have its row scalars, which go to the other buffer; the barrier
               // publishes both, and the reads for item it+1's first MFMAs and its -D
@@ -436,18 +455,18 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
               store_scalars(buf ^ 1);
               __syncthreads();
             }
-            if constexpr (i >= 57 && i < 61) load_nd(IC<0>{}, IC<i - 57>{}, buf ^ 1);
-            // block 0's softmax behind block 1's S, dP; block 1's behind block 0's dV, dK
-            if constexpr (slot == 1) {
-              soft_a(IC<0>{}, IC<j>{});
-              if constexpr (j >= 1) soft_b(IC<0>{}, IC<j - 1>{});
-            } else if constexpr (slot == 2) {
-              if constexpr (j == 0) soft_b(IC<0>{}, IC<15>{});
-              soft_a(IC<1>{}, IC<j>{});
-              if constexpr (j >= 1) soft_b(IC<1>{}, IC<j - 1>{});
-            } else if constexpr (slot == 3) {
-              if constexpr (j == 0) soft_b(IC<1>{}, IC<15>{});
-            }
+            if constexpr (i >= 121 && i < 125) load_nd(IC<0>{}, IC<i - 121>{}, buf ^ 1);
+            // block b's softmax: stage A of element j and stage B of element j-1 in slot
+            // sm_slot(b), stage B of element 15 at the first step of the next slot
+            unroll<NQB>([&](auto B) {
+              constexpr int qb = decltype(B)::v;
+              if constexpr (slot == sm_slot(qb)) {
+                soft_a(IC<qb>{}, IC<j>{});
+                if constexpr (j >= 1) soft_b(IC<qb>{}, IC<j - 1>{});
+              } else if constexpr (slot == sm_slot(qb) + 1 && j == 0) {
+                soft_b(IC<qb>{}, IC<15>{});
+              }
+            });
           });
     }
 

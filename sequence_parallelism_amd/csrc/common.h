@@ -154,7 +154,7 @@ struct AttnBwdArgs {
   void* dk;
   void* dv;
   // workspace regions
-  // row scalars of the dK/dV kernel, planes of rs_ld (Sq rounded up to 64) rows:
+  // row scalars of the dK/dV kernel, planes of rs_ld (Sq rounded up to its 128-row items) rows:
   // [Hq] lse log2(e), [Hq] -D (fp32 bits), then klo, khi (int32, the visible keys)
   uint32_t* rs;
   int32_t rs_ld;
