@@ -10,8 +10,8 @@
 // and H*D elements apart on the sequence-sharded side.  The kernel is pure data
 // movement and HBM bound: each thread moves 16-byte vectors (narrower only when
 // the run length or alignment forces it), a grid row per (g, s) pair keeps the
-// index arithmetic to one fast division per vector, and the packed side is
-// streamed with non-temporal stores.
+// index arithmetic to one fast division per vector, and both sides are streamed
+// with non-temporal loads and stores (nothing is read twice).
 #include "common.h"
 
 namespace {
@@ -71,14 +71,14 @@ __global__ __launch_bounds__(256) void permute_kernel(
   if (to_head) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u)
-      if (ok[u]) buf[u] = *reinterpret_cast<const V*>(src + so[u]);
+      if (ok[u]) buf[u] = __builtin_nontemporal_load(reinterpret_cast<const V*>(src + so[u]));
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u)
       if (ok[u]) __builtin_nontemporal_store(buf[u], reinterpret_cast<V*>(dst + po[u]));
   } else {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u)
-      if (ok[u]) buf[u] = *reinterpret_cast<const V*>(src + po[u]);
+      if (ok[u]) buf[u] = __builtin_nontemporal_load(reinterpret_cast<const V*>(src + po[u]));
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u)
       if (ok[u]) __builtin_nontemporal_store(buf[u], reinterpret_cast<V*>(dst + so[u]));
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void stripe_kernel(char* __restrict__ dst, con
   }
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u)
-    if (ok[u]) buf[u] = *reinterpret_cast<const V*>(src + (to_stripe ? co[u] : so[u]));
+    if (ok[u]) buf[u] = __builtin_nontemporal_load(reinterpret_cast<const V*>(src + (to_stripe ? co[u] : so[u])));
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u)
     if (ok[u]) __builtin_nontemporal_store(buf[u], reinterpret_cast<V*>(dst + (to_stripe ? so[u] : co[u])));
