@@ -241,7 +241,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
     dma16_at<(uint32_t)((u * TILE + 4 * i * 512) * 2)>(src.tile[u], vq, base);
   };
 
-  // Row scalars of an item (written by the dQ kernel), one row per lane, read one item
+  // Row scalars of an item (written by the dQ kernel), two rows per lane, read one item
   // ahead: wave w loads plane w, with no arithmetic on the value (that would stall the
   // pipeline it sits in for a whole memory latency), and stores it at the item's
   // publishing barrier.
