@@ -593,12 +593,21 @@ size_t n_dq_tiles(int64_t Sq) {
 
 // Item-range split of the dK/dV kernel for a call: 1 (none) unless its key blocks
 // (times key/value heads) give at most two workgroups per CU and its query tiles are
-// many; then chunks for about four workgroups per CU, at most 8.
-int bwd_kv_split(int64_t Sq, int64_t Sk, int32_t Hkv) {
+// many; then chunks for about one workgroup per CU, or four for a long triangular call
+// (a causal one whose keys reach past its first query row: its first key blocks see
+// many times the query tiles of its last ones, and only small chunks let the work
+// queues balance them), at most 8.  Otherwise more chunks cost more in partials and
+// their combine pass than they gain in balance.
+int bwd_kv_split(int64_t Sq, int64_t Sk, int32_t Hkv, bool triangular) {
   const int64_t wg = (int64_t)n_kv_blocks(Sk) * Hkv;
   const int cus = device_cu_count();
   if (wg == 0 || wg > 2 * (int64_t)cus || Sq < 2048) return 1;
-  return (int)std::min<int64_t>(8, (4 * (int64_t)cus + wg - 1) / wg);
+  const int64_t per_cu = triangular && Sq >= 8192 ? 4 : 1;
+  return (int)std::min<int64_t>(8, (per_cu * cus + wg - 1) / wg);
+}
+
+static bool kv_triangular(const AttnArgs& f) {
+  return f.causal && (int64_t)f.k_start + (int64_t)f.k_stride * (f.Sk - 1) > (int64_t)f.q_start;
 }
 
 size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D) {
@@ -608,7 +617,8 @@ size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv,
              + align256(sizeof(int))                                          // its slots per XCD
              + align256(NXCD * sizeof(int))                                   // dK/dV work queues
              + align256(n_dq_tiles(Sq) * sizeof(int));                        // dQ tile order
-  const int qs = bwd_dq_split(Sq, Sk, Hq), ks = bwd_kv_split(Sq, Sk, Hkv);
+  // the call's offsets are not known here: room for the larger (triangular) split
+  const int qs = bwd_dq_split(Sq, Sk, Hq), ks = bwd_kv_split(Sq, Sk, Hkv, true);
   if (qs > 1) n += align256((size_t)Hq * (size_t)((Sq + 255) / 256) * qs * 256 * HD * sizeof(float));
   if (ks > 1) n += align256((size_t)Hkv * n_kv_blocks(Sk) * ks * 2 * BKV * HD * sizeof(float));
   return n;
@@ -629,7 +639,7 @@ void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
   a.dq_order = reinterpret_cast<int*>(p);
   p += align256(n_dq_tiles(f.Sq) * sizeof(int));
   a.dq_split = bwd_dq_split(f.Sq, f.Sk, f.Hq);
-  a.kv_split = bwd_kv_split(f.Sq, f.Sk, f.Hkv);
+  a.kv_split = bwd_kv_split(f.Sq, f.Sk, f.Hkv, kv_triangular(f));
   a.dq_part = nullptr;
   a.kv_part = nullptr;
   if (a.dq_split > 1) {

@@ -374,7 +374,7 @@ int bwd_dq_split(int64_t Sq, int64_t Sk, int32_t Hq) {
   const int64_t wg = (int64_t)((Sq + 255) / 256) * Hq;
   const int cus = device_cu_count();
   if (wg == 0 || wg >= cus || Sk < 2048) return 1;
-  return (int)std::min<int64_t>(16, (4 * (int64_t)cus + wg - 1) / wg);
+  return (int)std::min<int64_t>(16, ((int64_t)cus + wg - 1) / wg);
 }
 
 // a must carry the workspace regions of attn_bwd_workspace_layout; the kernel also

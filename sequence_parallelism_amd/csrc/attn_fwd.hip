@@ -413,13 +413,14 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 }  // namespace
 
 // Key-range split of a call: 1 (none) unless its 256-row workgroups (times heads)
-// would leave CUs idle and its keys are many; then chunks for about four workgroups
-// per CU, at most 16.
+// would leave CUs idle and its keys are many; then chunks for about one workgroup per
+// CU, at most 16 (more chunks cost more in fp32 partials and their combine pass than
+// they gain in balance).
 int fwd_ksplit(int64_t Sq, int64_t Sk, int32_t Hq) {
   const int64_t wg = (int64_t)((Sq + 255) / 256) * Hq;
   const int cus = device_cu_count();
   if (wg == 0 || wg >= cus || Sk < 2048) return 1;
-  return (int)std::min<int64_t>(16, (4 * (int64_t)cus + wg - 1) / wg);
+  return (int)std::min<int64_t>(16, ((int64_t)cus + wg - 1) / wg);
 }
 
 // workspace: the query-tile order (sized for the 128-row tiles of the 4-wave

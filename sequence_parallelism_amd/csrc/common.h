@@ -173,7 +173,7 @@ struct AttnBwdArgs {
 };
 // key-range / item-range splits of the backward kernels for a call's sizes (1: none)
 int bwd_dq_split(int64_t Sq, int64_t Sk, int32_t Hq);
-int bwd_kv_split(int64_t Sq, int64_t Sk, int32_t Hkv);
+int bwd_kv_split(int64_t Sq, int64_t Sk, int32_t Hkv, bool triangular);
 size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv, int32_t D);
 // fills the workspace pointers of a from its base (layout of attn_bwd_workspace_bytes)
 void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base);
