@@ -86,9 +86,9 @@ static_assert(sdp_order(4) == 8 && sdp_order(5) == 4 && sdp_order(11) == 7 && sd
 // dV^T sums for the combine pass.
 typedef bf16 StageBuf[2][2 * BQ * HD];   // per buffer: Q [128 rows][128], dO [128][128] (swz16)
 typedef uint32_t ScalBuf[4][2][BQ];      // per buffer: lse log2(e), -D, klo, khi per row
-template <bool SPLIT>
+template <bool SPLIT, typename Fetch>
 __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles, int unit, StageBuf& stage,
-                                              ScalBuf& scal_s) {
+                                              ScalBuf& scal_s, Fetch&& fetch_unit, int& next_unit) {
   const AttnArgs& f = a.f;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -475,6 +475,10 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
   for (int it = it0; it < min(it1, n_full); ++it) run_item(IC<0>{}, it);
 #pragma unroll 1
   for (int it = max(it0, n_full); it < it1; ++it) run_item(IC<1>{}, it);
+  // a ticket of this XCD's queue for the next unit, taken now so that the atomic's
+  // round trip overlaps the stores below (its value is first used at the top of the
+  // kernel's unit loop)
+  if (threadIdx.x == 0) next_unit = fetch_unit();
   // the last accumulations (inline-assembly MFMAs) complete before any read below
   agpr_acc_fence();
   // ---- dK = scale dK^T, dV = dV^T (bf16), lane: key kl, d = 32db + 8g4 + 4hi + 0..3
@@ -533,21 +537,27 @@ __global__ __launch_bounds__(NWB * 64) void attn_bwd_main_kernel(AttnBwdArgs a, 
   const int xcc = (int)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)) & (NXCD - 1));
   // units per XCD: the schedule kernel's slots per XCD times the units per key block
   const int per_xcd = a.kv_slots[0] * a.f.Hkv * (SPLIT ? a.kv_split : 1);
+  // own queue first, then the others; an exhausted queue stays exhausted.  k: a ticket
+  // of the own queue already taken
+  auto unit_from = [&](int k) {
+    if (k < per_xcd) return xcc + NXCD * k;
+    for (int t = 1; t < NXCD; ++t) {
+      const int x = (xcc + t) & (NXCD - 1);
+      const int k2 = atomicAdd(&a.kv_next[x], 1);
+      if (k2 < per_xcd) return x + NXCD * k2;
+    }
+    return -1;
+  };
+  auto fetch_unit = [&]() { return atomicAdd(&a.kv_next[xcc], 1); };
+  int next_unit = -2;   // thread 0: the own-queue ticket taken during the previous unit's stores
   for (;;) {
     __syncthreads();   // the previous unit is done with the LDS (and with unit_s)
-    if (threadIdx.x == 0) {
-      int u = -1;
-      for (int t = 0; t < NXCD; ++t) {   // own queue first; an exhausted queue stays exhausted
-        const int x = (xcc + t) & (NXCD - 1);
-        const int k = atomicAdd(&a.kv_next[x], 1);
-        if (k < per_xcd) { u = x + NXCD * k; break; }
-      }
-      unit_s = u;
-    }
+    if (threadIdx.x == 0) unit_s = unit_from(next_unit != -2 ? next_unit : fetch_unit());
     __syncthreads();
     const int unit = __builtin_amdgcn_readfirstlane(unit_s);
     if (unit < 0) break;   // every wave sees the same unit: all leave together
-    attn_bwd_unit<SPLIT>(a, n_qtiles, unit, stage, scal_s);
+    next_unit = -2;
+    attn_bwd_unit<SPLIT>(a, n_qtiles, unit, stage, scal_s, fetch_unit, next_unit);
   }
 }
 

@@ -63,9 +63,33 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   const int row = qt * BR + wave * 32 + r32;
   const bool row_ok = row < f.Sq;
 
+  // ---- the unit's reads, issued together so that their latencies overlap: the row's
+  // position (all that its key range needs), the Q and dO fragments (B operands of
+  // S^T = K Q^T, dP^T = V dO^T: row r32, d = 16 kk + 8 hi + 0..7), the O elements at
+  // the same places and the row's lse (for D and the row scalars below).  A row past Sq
+  // reads row 0 and is inert: its lse is +inf, so P = dS = 0, and its dQ is not stored;
+  // no per-lane select, which would make the loads wait one by one.
+  const int pos_row = row_ok ? row_pos(f, row) : 0;
+  bf16x8 qf[8], df[8], of[8];
+  float l_raw = 0.f;
+  {
+    const int64_t off = rows_off(f.lq, row_ok ? row : 0, h) + 8 * hi;
+    const bf16* qsrc = reinterpret_cast<const bf16*>(f.q) + off;
+    const bf16* dsrc = reinterpret_cast<const bf16*>(a.dout) + off;
+    const bf16* osrc = reinterpret_cast<const bf16*>(f.o) + off;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      qf[kk] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * kk);
+      df[kk] = *reinterpret_cast<const bf16x8*>(dsrc + 16 * kk);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) of[kk] = *reinterpret_cast<const bf16x8*>(osrc + 16 * kk);
+    if (row_ok) l_raw = f.lse[(int64_t)h * f.lse_ld + row];
+  }
+
   // ---- visible keys: this lane's row sees local keys [klo, khi); the wave's summary
   int klo, khi;
-  const WaveKeys wk = wave_keys(f, row, row_ok, klo, khi);
+  const WaveKeys wk = wave_keys_at(f, row, row_ok, pos_row, klo, khi);
   if (lane == 0) { red[wave][0] = wk.lo; red[wave][1] = wk.hiex; }
   __syncthreads();
   int g_lo = red[0][0], g_hiex = red[0][1];
@@ -127,38 +151,16 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
 #pragma unroll
   for (int i = 0; i < 4; ++i) dqacc[i] = f32x16{};
 
-  // the first tile's DMA goes out before the fragment loads, so the two latencies overlap
+  // the first tile's DMA, in flight together with the loads issued above
   if (kb < ke)
     for (int s = 0; s < 2 * NL; ++s) dma_step(s, kb, 0);
 
-  // ---- Q and dO fragments (B operands of S^T = K Q^T, dP^T = V dO^T):
-  // row r32, d = 16 kk + 8 hi + 0..7 ------------------------------------------------
-  // (a row past Sq reads row 0 and is inert: its lse is +inf, so P = dS = 0, and its
-  // dQ is not stored; no per-lane select, which would make the loads wait one by one)
-  bf16x8 qf[8], df[8];
-  {
-    const int64_t off = rows_off(f.lq, row_ok ? row : 0, h) + 8 * hi;
-    const bf16* qsrc = reinterpret_cast<const bf16*>(f.q) + off;
-    const bf16* dsrc = reinterpret_cast<const bf16*>(a.dout) + off;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      qf[kk] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * kk);
-      df[kk] = *reinterpret_cast<const bf16x8*>(dsrc + 16 * kk);
-    }
-  }
   // row scalars: lse in log2 units (+inf for a row with no visible key, so that P = 0
   // there) and D = <dO, O> over the row, from the lane's dO fragments and the O
   // elements at the same places (fp32 dot products of bf16 pairs; the lane 32 apart
   // holds the other half of the row)
-  float l_raw = 0.f, dlt = 0.f;
+  float dlt = 0.f;
   {
-    const bf16* osrc = reinterpret_cast<const bf16*>(f.o) + rows_off(f.lq, row_ok ? row : 0, h) + 8 * hi;
-    bf16x8 of[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      of[kk] = *reinterpret_cast<const bf16x8*>(osrc + 16 * kk);
-    }
-    if (row_ok) l_raw = f.lse[(int64_t)h * f.lse_ld + row];
     auto dot2 = [](const bf16x2 x, const bf16x2 y, float c) { return __builtin_amdgcn_fdot2_f32_bf16(x, y, c, false); };
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {

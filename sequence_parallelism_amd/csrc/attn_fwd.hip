@@ -54,9 +54,10 @@ constexpr int NXCD = 8;          // MI355X dispatches workgroup i to XCD i % 8
 // has too few query tiles to fill the chip with 256-row workgroups.
 // SPLIT: the unit is chunk c of its tile's key range (a.ksplit chunks) and writes a
 // normalised partial O and LSE for the combine pass.
-template <bool O_F32, int NW, bool SPLIT>
+template <bool O_F32, int NW, bool SPLIT, typename Fetch>
 __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, int unit,
-                                              bf16 (&stage)[2][2 * TILE], int (&red)[NW][2]) {
+                                              bf16 (&stage)[2][2 * TILE], int (&red)[NW][2],
+                                              Fetch&& fetch_unit, int& next_unit) {
   constexpr int BR = 32 * NW;              // query rows per workgroup
   constexpr int NL = TILE / 8 / (NW * 64); // 64-lane DMA loads per wave per staged tile
   static_assert(NL * NW * 64 * 8 == TILE, "a staged tile is a whole number of loads per wave");
@@ -83,9 +84,21 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
 
   const bf16* __restrict__ qp = reinterpret_cast<const bf16*>(a.q);
 
+  // ---- the unit's two reads, issued together so that their latencies overlap: the
+  // row's position (all that its key range needs), then the Q fragment (B operand of
+  // S^T = K Q^T: row r32, d = 16*kk + 8*hi + 0..7; a row past Sq reads row 0, whose
+  // results are not stored).  The fragment is awaited after the first tile's DMA.
+  const int pos_row = row_ok ? row_pos(a, row) : 0;
+  bf16x8 qf[8];
+  {
+    const bf16* src = qp + rows_off(a.lq, row_ok ? row : 0, h) + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(src + 16 * kk);
+  }
+
   // ---- visible keys: this lane's row sees local keys [klo, khi); the wave's summary
   int klo, khi;
-  const WaveKeys wk = wave_keys(a, row, row_ok, klo, khi);
+  const WaveKeys wk = wave_keys_at(a, row, row_ok, pos_row, klo, khi);
   if (lane == 0) { red[wave][0] = wk.lo; red[wave][1] = wk.hiex; }
   __syncthreads();
   int g_lo = red[0][0], g_hiex = red[0][1];
@@ -149,24 +162,14 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
     }
   }
 
-  // the first tile's DMA goes out before the fragment loads, so the two latencies overlap
+  // the first tile's DMA, in flight together with the Q fragment loads issued above
   if (kb < ke)
     for (int s = 0; s < 2 * NL; ++s) dma_step(s, kb, 0);
 
-  // ---- Q fragment (B operand of S^T = K Q^T): row r32, d = 16*kk + 8*hi + 0..7
-  // (a row past Sq reads row 0; its results are not stored)
-  bf16x8 qf[8];
-  {
-    const bf16* src = qp + rows_off(a.lq, row_ok ? row : 0, h) + 8 * hi;
+  // the Q fragment consumed here, so that the compiler waits for its loads once, now,
+  // and not inside the tile loop (where its wait would also cover the tile DMA in flight)
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      qf[kk] = *reinterpret_cast<const bf16x8*>(src + 16 * kk);
-    }
-    // consumed here, so that the compiler waits for these loads once, now, and not
-    // inside the tile loop (where its wait would also cover the tile DMA in flight)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) asm volatile("" :: "v"(qf[kk]));
-  }
+  for (int kk = 0; kk < 8; ++kk) asm volatile("" :: "v"(qf[kk]));
 
   if (kb < ke) {
     wait_vmem();
@@ -261,6 +264,10 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
     __syncthreads();   // ... for every wave; this buffer is free again
   }
 
+  // a ticket of this XCD's queue for the next unit, taken now so that the atomic's
+  // round trip overlaps the epilogue (its value is first used at the top of the
+  // kernel's unit loop)
+  if (threadIdx.x == 0) next_unit = fetch_unit();
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 ---------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -306,21 +313,27 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnArgs a, int 
   __shared__ int unit_s;
   const int xcc = (int)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)) & (NXCD - 1));   // XCC_ID
   const int per_xcd = (n_units + NXCD - 1) / NXCD;
+  // own queue first, then the others; an exhausted queue stays exhausted.  k: a ticket
+  // of the own queue already taken
+  auto unit_from = [&](int k) {
+    if (k < per_xcd) return xcc + NXCD * k;
+    for (int t = 1; t < NXCD; ++t) {
+      const int x = (xcc + t) & (NXCD - 1);
+      const int k2 = atomicAdd(&a.q_next[x], 1);
+      if (k2 < per_xcd) return x + NXCD * k2;
+    }
+    return -1;
+  };
+  auto fetch_unit = [&]() { return atomicAdd(&a.q_next[xcc], 1); };
+  int next_unit = -2;   // thread 0: the own-queue ticket taken during the previous unit's epilogue
   for (;;) {
     __syncthreads();   // the previous unit is done with the LDS (and with unit_s)
-    if (threadIdx.x == 0) {
-      int u = -1;
-      for (int t = 0; t < NXCD; ++t) {   // own queue first; an exhausted queue stays exhausted
-        const int x = (xcc + t) & (NXCD - 1);
-        const int k = atomicAdd(&a.q_next[x], 1);
-        if (k < per_xcd) { u = x + NXCD * k; break; }
-      }
-      unit_s = u;
-    }
+    if (threadIdx.x == 0) unit_s = unit_from(next_unit != -2 ? next_unit : fetch_unit());
     __syncthreads();
     const int unit = __builtin_amdgcn_readfirstlane(unit_s);
     if (unit < 0) break;   // every wave sees the same unit: all leave together
-    attn_fwd_unit<O_F32, NW, SPLIT>(a, n_qtiles, unit, stage, red);
+    next_unit = -2;
+    attn_fwd_unit<O_F32, NW, SPLIT>(a, n_qtiles, unit, stage, red, fetch_unit, next_unit);
   }
 }
 

@@ -107,19 +107,26 @@ struct AttnArgs {
 __host__ __device__ __forceinline__ int floor_div(int x, int s) { return x >= 0 ? x / s : -((s - 1 - x) / s); }
 __host__ __device__ __forceinline__ int ceil_div(int x, int s) { return -floor_div(-x, s); }
 
+// The position_ids entry of local query row `row`'s global token (0 when the call is
+// not causal, which reads no position).
+__device__ __forceinline__ int row_pos(const AttnArgs& a, int row) {
+  return a.causal ? a.pos[a.q_start + a.q_stride * row] : 0;
+}
 // Keys visible to local query row `row` (< Sq), as a local key range [lo, hiex)
 // clipped to [0, Sk) (empty when hiex <= lo).  Causal with position_ids: the row's
 // global index gq and its document start gq - pos[gq] bound the visible global key
 // indices, gq - pos[gq] <= k_start + k_stride j <= gq; otherwise every key.  With
 // k_stride 1 the bounds are plain differences; a stripe divides by its stride.
-__device__ __forceinline__ void row_keys(const AttnArgs& a, int row, int& lo, int& hiex) {
+// row_keys_at takes the row's position already read (row_pos), so that a kernel can
+// issue that read beside its other loads.
+__device__ __forceinline__ void row_keys_at(const AttnArgs& a, int row, int pos_row, int& lo, int& hiex) {
   if (!a.causal) {
     lo = 0;
     hiex = a.Sk;
     return;
   }
   const int gq = a.q_start + a.q_stride * row;
-  const int ds = gq - a.pos[gq];
+  const int ds = gq - pos_row;
   if (a.k_stride == 1) {
     lo = ds - a.k_start;
     hiex = gq - a.k_start + 1;
@@ -129,6 +136,9 @@ __device__ __forceinline__ void row_keys(const AttnArgs& a, int row, int& lo, in
   }
   lo = max(lo, 0);
   hiex = min(hiex, a.Sk);
+}
+__device__ __forceinline__ void row_keys(const AttnArgs& a, int row, int& lo, int& hiex) {
+  row_keys_at(a, row, row_pos(a, row), lo, hiex);
 }
 
 // First local query row that sees local key j or a later one (causal): the smallest

@@ -163,10 +163,11 @@ constexpr int KBIG = 0x3fffffff;
 // the wave's summary: [lo, hiex) covers every key some row of the wave sees, [lomax,
 // himin) only keys that every row sees (empty rows make it empty).
 struct WaveKeys { int lo, hiex, lomax, himin; };
-__device__ __forceinline__ WaveKeys wave_keys(const AttnArgs& a, int row, bool row_ok, int& klo, int& khi) {
+__device__ __forceinline__ WaveKeys wave_keys_at(const AttnArgs& a, int row, bool row_ok, int pos_row, int& klo,
+                                                 int& khi) {
   klo = 0;
   khi = 0;
-  if (row_ok) row_keys(a, row, klo, khi);
+  if (row_ok) row_keys_at(a, row, pos_row, klo, khi);
   const bool any = row_ok && klo < khi;
   WaveKeys w;
   w.lo = __builtin_amdgcn_readfirstlane(wave_min(any ? klo : KBIG));
@@ -174,6 +175,9 @@ __device__ __forceinline__ WaveKeys wave_keys(const AttnArgs& a, int row, bool r
   w.lomax = __builtin_amdgcn_readfirstlane(wave_max(row_ok ? klo : -KBIG));
   w.himin = __builtin_amdgcn_readfirstlane(wave_min(row_ok ? khi : KBIG));
   return w;
+}
+__device__ __forceinline__ WaveKeys wave_keys(const AttnArgs& a, int row, bool row_ok, int& klo, int& khi) {
+  return wave_keys_at(a, row, row_ok, row_ok ? row_pos(a, row) : 0, klo, khi);
 }
 
 }  // namespace gfx950
