@@ -29,11 +29,11 @@
 //                 dP the previous slot finished (exp2, products, bf16 packing).  The
 //                 per-item bookkeeping (the next items' addresses, the publishing
 //                 barrier, the row scalars) is paid once per 128 MFMAs.
-// Query tiles that cannot see the key block are not visited (the first visible
-// tile follows from the block's first key, the last from a binary search over
-// document starts).  Fully visible tiles run first, without any masking work; the
-// few boundary tiles (the causal diagonal, a document boundary, a partial tile)
-// run after them with the mask folded into the row log-sum-exp.
+// Query tiles that cannot see the key block are not visited (the schedule kernel
+// works out each block's visible and fully visible tiles, schedule.hip).  Fully
+// visible tiles run first, without any masking work; the few boundary tiles (the
+// causal diagonal, a document boundary, a partial tile) run after them with the mask
+// folded into the row log-sum-exp.
 #include <algorithm>
 
 #include "gfx950.h"
@@ -105,13 +105,18 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
   const int kw0 = k0 + wave * 32;                       // this wave's first key
   const int kl = kw0 + r32;                             // this lane's key (B-operand column)
   const bool key_ok = kl < f.Sk;
-  const int k_last = min(k0 + BKV, f.Sk) - 1;           // the block's last key
   const int grp = f.Hq / f.Hkv;
   const float sl2 = f.scale * USP_LOG2E;
 
   const bf16* __restrict__ kp = reinterpret_cast<const bf16*>(f.k);
   const bf16* __restrict__ vp = reinterpret_cast<const bf16*>(f.v);
 
+  // The query tiles that can see the block, [t0, t1), and among them the fully visible
+  // ones [f0, f1) (every row valid, every key of the block valid, every (row, key) pair
+  // unmasked), worked out by the schedule kernel; read first, so that waiting for them
+  // leaves the K and V loads below in flight.
+  const int4 rng = *reinterpret_cast<const int4*>(a.kv_range + 4 * kbi);
+  __builtin_amdgcn_sched_barrier(0);
   // K and V fragments of this lane's key (B operands of S and dP): d = 16kk + 8hi + 0..7
   bf16x8 kf[8], vf[8];
   {
@@ -122,10 +127,6 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
       kf[kk] = key_ok ? *reinterpret_cast<const bf16x8*>(kp + off + 16 * kk) : z;
       vf[kk] = key_ok ? *reinterpret_cast<const bf16x8*>(vp + off + 16 * kk) : z;
     }
-    // consumed here, so that the compiler waits for these loads once, now, and not
-    // inside the item loop (where its wait would also cover the tile DMA in flight)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) asm volatile("" :: "v"(kf[kk]), "v"(vf[kk]));
   }
   // ---- per-lane LDS offsets, swizzled ------------------------------------------------
   // Logical chunk 2k + hi of row r sits at physical chunk (2k + hi) ^ swz(r) = 2k ^ t
@@ -151,37 +152,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
     }
   }
 
-  // ---- query tiles that can see the block: [t0, t1) ------------------------------
-  // and among them the fully visible ones [f0, f1): every row valid, every key of
-  // the block valid, and every (row, key) pair unmasked.  A row's visible keys
-  // [lo, hiex) (row_keys) have both ends nondecreasing along the rows, so the causal
-  // bound needs the tile's first row to see the block's last key, and the document
-  // bound needs the last row's first visible key at or before the block's first.
-  int t0 = 0, t1 = n_qtiles, f0 = 0, f1 = min(n_qtiles, f.Sq / BQ);
-  if (f.causal) {
-    t0 = min(first_row_seeing(f, k0) / BQ, n_qtiles);
-    // first tile whose first row's visible keys start after the block's last key
-    int lo_t = t0, hi_t = n_qtiles;
-    while (lo_t < hi_t) {
-      const int mid = (lo_t + hi_t) >> 1;
-      int lo_k, hiex_k;
-      row_keys(f, mid * BQ, lo_k, hiex_k);
-      if (lo_k > k_last) hi_t = mid; else lo_t = mid + 1;
-    }
-    t1 = lo_t;
-    f0 = max(t0, (first_row_seeing(f, k_last) + BQ - 1) / BQ);
-    // first complete tile whose last row's visible keys start after the block's first key
-    lo_t = f0;
-    hi_t = max(f1, f0);
-    while (lo_t < hi_t) {
-      const int mid = (lo_t + hi_t) >> 1;
-      int lo_k, hiex_k;
-      row_keys(f, mid * BQ + BQ - 1, lo_k, hiex_k);
-      if (lo_k > k0) hi_t = mid; else lo_t = mid + 1;
-    }
-    f1 = min(lo_t, t1);
-  }
-  if (k0 + BKV > f.Sk || f1 < f0) f1 = f0;   // no fully visible tile
+  const int t0 = rng.x, t1 = rng.y, f0 = rng.z, f1 = rng.w;
   // visiting order for every head: the fully visible tiles [f0, f1), then the others,
   // [t0, m1) and [m2, t1)
   const int m1 = f1 > f0 ? f0 : t1, m2 = f1 > f0 ? f1 : t1;
@@ -334,6 +305,11 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
     unroll<PF>([&](auto I) { ops[decltype(I)::v] = op_at(I, 0); });
     unroll<4>([&](auto G4) { load_nd(IC<0>{}, G4, 0); });
   }
+  // K and V consumed here, after item 0's DMA (with which they were in flight), so that
+  // the compiler waits for them once, now, and not inside the item loop (where its wait
+  // would also cover the tile DMA in flight)
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) asm volatile("" :: "v"(kf[kk]), "v"(vf[kk]));
 
   // one item; MASK: a boundary item, whose hidden (row, key) pairs get the row
   // log-sum-exp +inf so that P and dS vanish there
@@ -626,6 +602,7 @@ size_t attn_bwd_workspace_bytes(int64_t Sq, int64_t Sk, int32_t Hq, int32_t Hkv,
              + align256(NXCD * n_kv_blocks(Sk) * sizeof(int))                 // key-block order by XCD
              + align256(sizeof(int))                                          // its slots per XCD
              + align256(NXCD * sizeof(int))                                   // dK/dV work queues
+             + align256(4 * n_kv_blocks(Sk) * sizeof(int))                    // key blocks' query tiles
              + align256(n_dq_tiles(Sq) * sizeof(int));                        // dQ tile order
   // the call's offsets are not known here: room for the larger (triangular) split
   const int qs = bwd_dq_split(Sq, Sk, Hq), ks = bwd_kv_split(Sq, Sk, Hkv, true);
@@ -646,6 +623,8 @@ void attn_bwd_workspace_layout(AttnBwdArgs& a, void* base) {
   p += align256(sizeof(int));
   a.kv_next = reinterpret_cast<int*>(p);
   p += align256(NXCD * sizeof(int));
+  a.kv_range = reinterpret_cast<int*>(p);
+  p += align256(4 * n_kv_blocks(f.Sk) * sizeof(int));
   a.dq_order = reinterpret_cast<int*>(p);
   p += align256(n_dq_tiles(f.Sq) * sizeof(int));
   a.dq_split = bwd_dq_split(f.Sq, f.Sk, f.Hq);
@@ -672,7 +651,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   if (e != hipSuccess || f.Sk == 0) return e;
   const int n_ktiles = (f.Sk + BKV - 1) / BKV;
   const int n_qtiles = (f.Sq + BQ - 1) / BQ;
-  e = launch_schedule_kv_blocks(f, n_ktiles, BKV, BQ, a.kv_order, a.kv_slots, a.kv_next, stream);
+  e = launch_schedule_kv_blocks(f, n_ktiles, BKV, BQ, a.kv_order, a.kv_slots, a.kv_next, a.kv_range, stream);
   if (e != hipSuccess) return e;
   // one persistent workgroup per CU (the kernel's registers allow one per CU)
   const int n_units = n_ktiles * f.Hkv * a.kv_split;

@@ -171,6 +171,7 @@ struct AttnBwdArgs {
   int* kv_order;       // key blocks of the dK/dV kernel by XCD: slot x + 8 i = XCD x's i-th (-1: none)
   int* kv_slots;       // [1]: slots per XCD in kv_order (written by the schedule kernel)
   int* kv_next;        // the dK/dV kernel's per-XCD work queues [8] (zeroed by its schedule kernel)
+  int* kv_range;       // [key blocks][4]: t0, t1, f0, f1 of each key block (its schedule kernel)
   int* dq_order;       // query tiles of the dQ kernel, heaviest first
   // split key ranges of the dQ kernel (dq_split > 1): partial dQ^T sums per chunk,
   // dq_part [Hq][tiles][dq_split][256][128] fp32, summed by a combine pass
@@ -197,9 +198,10 @@ int attn_bwd_dq_rows_per_tile();
 // Heaviest-first launch orders (schedule.hip): key blocks of bkv keys seen by bq-row
 // query tiles (dK/dV kernel), and query tiles of br rows (forward and dQ kernels).
 // key blocks grouped by XCD (order: NXCD * n_blocks entries; slots_out[0]: slots per XCD;
-// and NXCD work-queue counters `next` that the launch zeroes)
+// and NXCD work-queue counters `next` that the launch zeroes), and each block's query
+// tiles (range: 4 n_blocks entries t0, t1, f0, f1, as kv_block_tiles in schedule.hip)
 hipError_t launch_schedule_kv_blocks(const AttnArgs& a, int n_blocks, int bkv, int bq, int* order, int* slots_out,
-                                     int* next, hipStream_t s);
+                                     int* next, int* range, hipStream_t s);
 // (q_next: NULL, or NXCD work-queue counters that the launch also zeroes)
 hipError_t launch_schedule_q_tiles(const AttnArgs& a, int n_tiles, int br, int* order, int* q_next, hipStream_t s);
 

@@ -6,8 +6,9 @@
 // heavy workgroups start late and run alone.  Launching them in decreasing order of
 // work keeps every CU busy to the end.
 //
-// One workgroup per call: each unit's work (its number of visible tiles) comes from
-// position_ids the same way the kernels derive their tile ranges; units are then
+// One workgroup per call: each unit's work comes from position_ids the same way the
+// kernels derive their tile ranges (the dK/dV kernel's key blocks take theirs from
+// here: the number of visible tiles is the work); units are then
 // bucket-sorted by work, heaviest first, into an int32 order array (the dK/dV kernel's
 // key blocks first grouped into one contiguous key range per XCD).  Units of equal
 // bucket keep no particular order; results never depend on the order beyond fp32
@@ -20,7 +21,7 @@ constexpr int NT = 1024;        // threads of the one workgroup
 constexpr int NB = 2048;        // work buckets
 constexpr int MAXU = 12288;     // units sorted in LDS; larger launches keep natural order
 
-constexpr int MAXT = 8192;
+constexpr int MAXT = 8192;      // query tiles whose first visible keys the dK/dV schedule keeps in LDS
 constexpr int NWAVE = NT / 64;
 
 // Inclusive prefix sum of v over the workgroup's NT threads in thread order: a scan
@@ -40,26 +41,50 @@ __device__ T block_incl_scan(T v, T* wsum) {
   for (int i = 0; i < w; ++i) before += wsum[i];
   __syncthreads();   // wsum may be reused
   return v + before;
-}      // query tiles whose first visible key the dK/dV schedule keeps in LDS
+}
 
-// Work of key block b of BKV keys for the dK/dV kernel: the number of BQ-row query
-// tiles that can see it (the kernel visits these for every query head of the group).
-// tile_lo: the first visible key of each tile's first row (row_keys), or null to read
-// it from position_ids at every step of the search.
-__device__ int kv_block_work(const AttnArgs& f, int b, int bkv, int bq, int n_qtiles, const int* tile_lo) {
-  if (!f.causal) return n_qtiles;
+// Query tiles of bq rows that key block b of bkv keys meets in the dK/dV kernel, as
+// {t0, t1, f0, f1}: tiles [t0, t1) can see the block (the kernel visits these for every
+// query head of the group, so t1 - t0 is the block's work), and among them the tiles
+// [f0, f1) see all of it: every row valid, every key of the block valid, and every
+// (row, key) pair unmasked (f1 = f0: none).  A row's visible keys [lo, hiex)
+// (row_keys) have both ends nondecreasing along the rows, so a tile sees the block when
+// its first row's first visible key is at or before the block's last key (t0 follows
+// from the causal bound, t1 from a binary search), and sees all of it when its first
+// row sees the block's last key (f0) and its last row's first visible key is at or
+// before the block's first key (a second binary search, over the complete tiles).
+// first_lo / last_lo: the first visible key of each tile's first row and of each
+// complete tile's last row, or null to read position_ids at every step of the search.
+__device__ int4 kv_block_tiles(const AttnArgs& f, int b, int bkv, int bq, int n_qtiles, const int* first_lo,
+                               const int* last_lo) {
   const int k0 = b * bkv;
   const int k_last = min(k0 + bkv, f.Sk) - 1;
-  const int t0 = min(first_row_seeing(f, k0) / bq, n_qtiles);
-  int lo = t0, hi = n_qtiles;   // first tile whose first row's visible keys start after k_last
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    int lo_k, hiex_k;
-    if (tile_lo) lo_k = tile_lo[mid];
-    else row_keys(f, mid * bq, lo_k, hiex_k);
-    if (lo_k > k_last) hi = mid; else lo = mid + 1;
+  int t0 = 0, t1 = n_qtiles, f0 = 0, f1 = min(n_qtiles, f.Sq / bq);
+  if (f.causal) {
+    auto tile_lo = [&](const int* cache, int t, int row) {
+      if (cache) return cache[t];
+      int lo_k, hiex_k;
+      row_keys(f, row, lo_k, hiex_k);
+      return lo_k;
+    };
+    t0 = min(first_row_seeing(f, k0) / bq, n_qtiles);
+    int lo = t0, hi = n_qtiles;   // first tile whose first row's visible keys start after k_last
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_lo(first_lo, mid, mid * bq) > k_last) hi = mid; else lo = mid + 1;
+    }
+    t1 = lo;
+    f0 = max(t0, (first_row_seeing(f, k_last) + bq - 1) / bq);
+    lo = f0;                      // first complete tile whose last row's visible keys start after k0
+    hi = max(f1, f0);
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_lo(last_lo, mid, mid * bq + bq - 1) > k0) hi = mid; else lo = mid + 1;
+    }
+    f1 = min(lo, t1);
   }
-  return lo - t0;
+  if (k0 + bkv > f.Sk || f1 < f0) f1 = f0;   // a partial block, or no fully visible tile
+  return make_int4(t0, t1, f0, f1);
 }
 
 // Work of query tile t of BR rows for the forward and dQ kernels: the number of keys
@@ -119,36 +144,47 @@ __global__ __launch_bounds__(NT) void schedule_q_kernel(AttnArgs f, int n, int b
 // L2); segment x's blocks, heaviest first, go to slots x, x + NXCD, x + 2 NXCD, ...
 // of `order` (-1 past the segment's end), and slots_out[0] gets the longest segment's
 // length.  `order` holds NXCD * n entries; next[0..7], the work queues of the kernel
-// that follows, are zeroed.
+// that follows, are zeroed; range[4 b .. 4 b + 3] gets block b's query tiles
+// (kv_block_tiles), so that the kernel's units need not search for them.
+// One workgroup, except past MAXU blocks: then one thread per block over as many
+// workgroups as that takes, in natural order.
 constexpr int NXCD = 8;
 constexpr int NBS = NB / NXCD;   // work buckets per segment
 __global__ __launch_bounds__(NT) void schedule_kv_xcd_kernel(AttnArgs f, int n, int bkv, int bq, int n_qtiles,
                                                              int* __restrict__ order, int* __restrict__ slots_out,
-                                                             int* __restrict__ next) {
+                                                             int* __restrict__ next, int4* __restrict__ range) {
   __shared__ int w_s[MAXU];      // work, then (segment << 27) | work
   __shared__ int start[NB];
   __shared__ int64_t part_w[NWAVE], total_s;
   __shared__ int wsum_s[NWAVE];
-  __shared__ int tile_lo_s[MAXT];
+  __shared__ int first_lo_s[MAXT], last_lo_s[MAXT];
   __shared__ int wmax_s, seg_start[NXCD + 1];
   const int tid = threadIdx.x;
-  if (tid < NXCD) next[tid] = 0;
+  if (blockIdx.x == 0 && tid < NXCD) next[tid] = 0;
   if (n > MAXU) {   // natural order, interleaved over the XCDs
     const int per = (n + NXCD - 1) / NXCD;
-    for (int u = tid; u < NXCD * per; u += NT) order[u] = u < n ? u : -1;
-    if (tid == 0) slots_out[0] = per;
+    for (int u = blockIdx.x * NT + tid; u < NXCD * per; u += gridDim.x * NT) {
+      order[u] = u < n ? u : -1;
+      if (u < n) range[u] = kv_block_tiles(f, u, bkv, bq, n_qtiles, nullptr, nullptr);
+    }
+    if (blockIdx.x == 0 && tid == 0) slots_out[0] = per;
     return;
   }
   for (int b = tid; b < NB; b += NT) start[b] = 0;
   if (tid == 0) wmax_s = 0;
-  // the first visible key of every query tile, read once (all loads in flight together)
-  // so that the binary searches below run in LDS
+  // the first visible key of every query tile's first row and of every complete tile's
+  // last row, read once (all loads in flight together) so that the binary searches
+  // below run in LDS
   const bool lds_lo = f.causal && n_qtiles <= MAXT;
   if (lds_lo) {
     for (int t = tid; t < n_qtiles; t += NT) {
       int lo_k, hiex_k;
       row_keys(f, t * bq, lo_k, hiex_k);
-      tile_lo_s[t] = lo_k;
+      first_lo_s[t] = lo_k;
+      if (t * bq + bq <= f.Sq) {
+        row_keys(f, t * bq + bq - 1, lo_k, hiex_k);
+        last_lo_s[t] = lo_k;
+      }
     }
   }
   __syncthreads();
@@ -158,7 +194,10 @@ __global__ __launch_bounds__(NT) void schedule_kv_xcd_kernel(AttnArgs f, int n, 
   int wmax = 0;
   int64_t mine = 0;
   for (int u = u0; u < u1; ++u) {
-    const int w = kv_block_work(f, u, bkv, bq, n_qtiles, lds_lo ? tile_lo_s : nullptr);
+    const int4 r = lds_lo ? kv_block_tiles(f, u, bkv, bq, n_qtiles, first_lo_s, last_lo_s)
+                          : kv_block_tiles(f, u, bkv, bq, n_qtiles, nullptr, nullptr);
+    range[u] = r;
+    const int w = r.y - r.x;
     w_s[u] = w;
     wmax = max(wmax, w);
     mine += w;
@@ -215,11 +254,12 @@ __global__ __launch_bounds__(NT) void schedule_kv_xcd_kernel(AttnArgs f, int n, 
 }  // namespace
 
 hipError_t launch_schedule_kv_blocks(const AttnArgs& a, int n_blocks, int bkv, int bq, int* order,
-                                     int* slots_out, int* next, hipStream_t stream) {
+                                     int* slots_out, int* next, int* range, hipStream_t stream) {
   if (n_blocks <= 0) return hipSuccess;
   const int n_qtiles = (a.Sq + bq - 1) / bq;
-  hipLaunchKernelGGL(schedule_kv_xcd_kernel, dim3(1), dim3(NT), 0, stream, a, n_blocks, bkv, bq, n_qtiles,
-                     order, slots_out, next);
+  const int grid = n_blocks > MAXU ? (n_blocks + NT - 1) / NT : 1;
+  hipLaunchKernelGGL(schedule_kv_xcd_kernel, dim3(grid), dim3(NT), 0, stream, a, n_blocks, bkv, bq, n_qtiles,
+                     order, slots_out, next, reinterpret_cast<int4*>(range));
   return hipGetLastError();
 }
 

@@ -107,3 +107,41 @@ def test_causal_beyond_schedule_tile_table(usp):
     check_grad(dq[a:b].cpu(), rq, "dq")
     check_grad(dk[a:b].cpu(), rk, "dk")
     check_grad(dv[a:b].cpu(), rv, "dv")
+
+
+def test_causal_query_block_past_sorted_key_blocks(usp):
+    """A ring-style causal call whose key block is more than 12288 key blocks long (a
+    ragged last block included): the dK/dV schedule then keeps natural order and works
+    out every block's query tiles from position_ids alone.  The 200 query rows are the
+    last tokens of the sequence, inside its last document of 1000 tokens; every key
+    before that document gets dK = dV = 0 exactly (no row sees it, and every unit writes
+    its block over the NaN fill), and the document's keys, the output and dQ match the
+    oracle run on that document alone."""
+    T, L, Sq = 12300 * 128 + 77, 1000, 200
+    say("causal query block past the sorted key blocks", T, L, Sq)
+    lengths = [T - L - 333, 333, L]
+    pos = inputs.position_ids(lengths)
+    gen = inputs.generator(55)
+    q, do = inputs.normal((Sq, 2, 128), gen), inputs.normal((Sq, 2, 128), gen)
+    k, v = inputs.normal((T, 1, 128), gen), inputs.normal((T, 1, 128), gen)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    posd = torch.from_numpy(pos).to(DEV)
+    qa = T - Sq
+    o, lse = usp.blockattn_fwd(qd, kd, vd, posd, q_start=qa, k_start=0, causal=True)
+    nan = lambda t: torch.full_like(t, float("nan"))
+    dq, dk, dv = usp.blockattn_bwd(qd, kd, vd, o, lse, dod, posd, q_start=qa, k_start=0, causal=True,
+                                   dq=nan(qd), dk=nan(kd), dv=nan(vd))
+    torch.cuda.synchronize()
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t).all()), name
+    assert not bool(dk[:T - L].any()) and not bool(dv[:T - L].any()), "keys no row sees"
+    dpos = np.arange(L, dtype=np.int32)
+    args = (f64(q), f64(k[T - L:]), f64(v[T - L:]))
+    kw = dict(pos=dpos, q_start=L - Sq, k_start=0, causal=True)
+    ref_o, ref_l = oracle.attention_fwd(*args, **kw)
+    check_o(o.cpu(), ref_o, "o")
+    check_lse(lse.cpu(), ref_l, "lse")
+    rq, rk, rv = oracle.attention_bwd(*args, f64(do), **kw)
+    check_grad(dq.cpu(), rq, "dq")
+    check_grad(dk[T - L:].cpu(), rk, "dk")
+    check_grad(dv[T - L:].cpu(), rv, "dv")
