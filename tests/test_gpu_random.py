@@ -13,6 +13,8 @@ test_gpu_parity.py: O within 2e-2 abs + 1e-2 rel, LSE within 1e-3, gradients wit
 5e-2 of the reference's max-norm.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -24,8 +26,10 @@ pytestmark = pytest.mark.gpu
 
 O_ATOL, O_RTOL, LSE_ATOL, GRAD_REL = 2e-2, 1e-2, 1e-3, 5e-2
 DEV = "cuda:0"
-N_CASES = 48          # small calls (S <= 1600): the 4-wave kernels
-N_SPLIT = 16          # S in [2048, 4096], 1-4 query heads: the split key / query ranges
+# case counts (environment overrides for longer sweeps; the defaults run in about a minute)
+N_CASES = int(os.environ.get("USP_RANDOM_CASES", "48"))        # small calls (S <= 1600)
+N_SPLIT = int(os.environ.get("USP_RANDOM_SPLIT_CASES", "16"))  # S in [2048, 4096], 1-4 query
+                                                               # heads: split key / query ranges
 
 
 def f64(t):
@@ -98,7 +102,7 @@ def test_random_call_fwd_bwd(usp, i, split):
 
 # ---- re-layouts: bit-exact against the oracle's index map -------------------------------
 
-N_PERM = 24
+N_PERM = int(os.environ.get("USP_RANDOM_PERMUTE_CASES", "24"))
 
 
 def draw_permute(i):
@@ -139,7 +143,7 @@ def test_random_permute_bitexact(usp, i):
 
 # ---- lse_merge: against the oracle's cumulative-softmax merge ---------------------------
 
-N_MERGE = 12
+N_MERGE = int(os.environ.get("USP_RANDOM_MERGE_CASES", "12"))
 
 
 @pytest.mark.parametrize("i", range(N_MERGE))
@@ -174,7 +178,7 @@ def test_random_lse_merge(usp, i):
 
 # ---- fused Ulysses entry points: bit-identical to the explicit re-layout chain ----------
 
-N_FUSED = 10
+N_FUSED = int(os.environ.get("USP_RANDOM_FUSED_CASES", "10"))
 
 
 @pytest.mark.parametrize("i", range(N_FUSED))
