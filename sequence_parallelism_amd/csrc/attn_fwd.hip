@@ -272,7 +272,45 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_out = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * USP_LN2 : -INFINITY;
-  if (row_ok) {
+  if constexpr (!SPLIT && !O_F32) {
+    // bf16 O through LDS, so that the stores write whole rows: the lane's 16 pieces of
+    // 8 bytes sit in 32 different rows, and each store of them would touch 32 cache
+    // lines.  Wave w stages its 32 rows x 256 bytes in its own 8 KB of stage buffer 0
+    // (free: every wave is past the last tile's barrier, no DMA is in flight, and the
+    // next unit writes the stage only after the barriers at the top of the kernel's
+    // loop), with the 16-byte chunks of row r XOR-swizzled by r % 16; it reads back 16
+    // bytes per lane, 4 rows per read, and stores 4 whole rows per instruction.
+    char* wl = reinterpret_cast<char*>(&stage[0][0]) + wave * (32 * HD * 2);
+    // (the lane index, pinned here so that the addresses below are computed here and
+    // not hoisted above the tile loop, where they would hold registers through it)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int wr = ln & 31;
+    char* wrow = wl + wr * (HD * 2) + 8 * (ln >> 5);
+    const int wsw = swz16(wr);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const bf16x4 ov = {(bf16)(oacc[db][4 * g4 + 0] * inv), (bf16)(oacc[db][4 * g4 + 1] * inv),
+                           (bf16)(oacc[db][4 * g4 + 2] * inv), (bf16)(oacc[db][4 * g4 + 3] * inv)};
+        // columns 32db + 8g4 + 4hi + 0..3 of row r32: logical chunk 4db + g4, half hi
+        *reinterpret_cast<bf16x4*>(wrow + (((4 * db + g4) ^ wsw) << 4)) = ov;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own writes, read back below
+    // rows 4k + lane/16 of the wave, chunk lane % 16; a tile never crosses a block of
+    // the row layout, so the rows are one row stride apart
+    const int c = ln & 15, orow0 = qt * BR + wave * 32 + (ln >> 4);
+    bf16* op = reinterpret_cast<bf16*>(a.o) + rows_off(a.lq, orow0, h) + 8 * c;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int rr = 4 * k + (ln >> 4);
+      const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(wl + rr * (HD * 2) + ((c ^ swz16(rr)) << 4));
+      if (orow0 + 4 * k < a.Sq) *reinterpret_cast<bf16x8*>(op + 4 * k * a.lq.row_stride) = v8;
+    }
+    if (row_ok && hi == 0) a.lse[(int64_t)h * a.lse_ld + row] = lse_out;
+  } else if (row_ok) {
     const int64_t slot = ((int64_t)h * n_qtiles + qt) * nch + chunk;   // partial of this chunk
     const int rr = wave * 32 + r32;
     const int64_t obase = SPLIT ? (slot * BR + rr) * HD : rows_off(a.lq, row, h);
@@ -283,14 +321,8 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
         const int d = 32 * db + 8 * g4 + 4 * hi;
         const f32x4 val = {oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv,
                            oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
-        if (SPLIT) {
-          *reinterpret_cast<f32x4*>(a.o_part + obase + d) = val;
-        } else if (O_F32) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + obase + d) = val;
-        } else {
-          const bf16x4 ov = {(bf16)val[0], (bf16)val[1], (bf16)val[2], (bf16)val[3]};
-          *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.o) + obase + d) = ov;
-        }
+        if (SPLIT) *reinterpret_cast<f32x4*>(a.o_part + obase + d) = val;
+        else *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + obase + d) = val;
       }
     }
     if (hi == 0) {
