@@ -477,21 +477,53 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
     }
     return;
   }
-  if (key_ok) {
-    const int64_t base = rows_off(f.lk, kl, hk);
-    bf16* dkp = reinterpret_cast<bf16*>(a.dk) + base;
-    bf16* dvp = reinterpret_cast<bf16*>(a.dv) + base;
+  // Through LDS, so that the stores write whole rows (the lane's 8-byte pieces sit in
+  // 32 different key rows).  Wave w stages its 32 keys' dK rows, then their dV rows
+  // (256 bytes each), in its own 16 KB of the stage buffer the last item did not use:
+  // that buffer holds only the last item's fetch of itself, which every wave awaited
+  // before the item's publishing barrier, and no wave reads it after the barrier that
+  // opened the last item (the next unit writes the stage only after the barriers at
+  // the top of the kernel's loop).  16-byte chunks of row r are XOR-swizzled by r % 16;
+  // each lane reads back 16 bytes, 4 rows per read, and each store writes 4 whole rows.
+  {
+    char* wl = reinterpret_cast<char*>(&stage[(it1 - it0) & 1][0]) + wave * (2 * 32 * HD * 2);
+    // (the lane index, pinned here so that the addresses below are computed here and
+    // not hoisted above the item loop, where they would hold registers through it)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int wr = ln & 31;
+    char* wrow = wl + wr * (HD * 2) + 8 * (ln >> 5);
+    const int wsw = swz16(wr);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * db + 8 * g4 + 4 * hi;
         const bf16x4 kv = {(bf16)(dka[db][4 * g4] * f.scale), (bf16)(dka[db][4 * g4 + 1] * f.scale),
                            (bf16)(dka[db][4 * g4 + 2] * f.scale), (bf16)(dka[db][4 * g4 + 3] * f.scale)};
         const bf16x4 vv = {(bf16)dva[db][4 * g4], (bf16)dva[db][4 * g4 + 1], (bf16)dva[db][4 * g4 + 2],
                            (bf16)dva[db][4 * g4 + 3]};
-        *reinterpret_cast<bf16x4*>(dkp + d) = kv;
-        *reinterpret_cast<bf16x4*>(dvp + d) = vv;
+        // columns 32db + 8g4 + 4hi + 0..3 of key row r32: logical chunk 4db + g4, half hi
+        const int off = ((4 * db + g4) ^ wsw) << 4;
+        *reinterpret_cast<bf16x4*>(wrow + off) = kv;
+        *reinterpret_cast<bf16x4*>(wrow + 32 * HD * 2 + off) = vv;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own writes, read back below
+    // key rows 4k + lane/16 of the wave, chunk lane % 16; a key block never crosses a
+    // block of the row layout, so the rows are one row stride apart
+    const int c = ln & 15, key0 = kw0 + (ln >> 4);
+    const int64_t base = rows_off(f.lk, key0, hk) + 8 * c;
+    bf16* dkp = reinterpret_cast<bf16*>(a.dk) + base;
+    bf16* dvp = reinterpret_cast<bf16*>(a.dv) + base;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int rr = 4 * k + (ln >> 4);
+      const int roff = rr * (HD * 2) + ((c ^ swz16(rr)) << 4);
+      const bf16x8 k8 = *reinterpret_cast<const bf16x8*>(wl + roff);
+      const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(wl + 32 * HD * 2 + roff);
+      if (key0 + 4 * k < f.Sk) {
+        *reinterpret_cast<bf16x8*>(dkp + 4 * k * f.lk.row_stride) = k8;
+        *reinterpret_cast<bf16x8*>(dvp + 4 * k * f.lk.row_stride) = v8;
       }
     }
   }

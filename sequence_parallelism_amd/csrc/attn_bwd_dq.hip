@@ -303,17 +303,40 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
     }
     return;
   }
-  if (row_ok) {
-    bf16* dqp = reinterpret_cast<bf16*>(a.dq) + rows_off(f.lq, row, h);
+  // Through LDS, so that the stores write whole rows (the lane's 8-byte pieces sit in
+  // 32 different rows): wave w stages its 32 rows x 256 bytes in its own 8 KB of the
+  // stage (free: every wave is past the last tile's barrier and no DMA is in flight),
+  // 16-byte chunks of row r XOR-swizzled by r % 16, reads back 16 bytes per lane and
+  // stores 4 whole rows per instruction.
+  {
+    char* wl = reinterpret_cast<char*>(&stage[0][0]) + wave * (32 * HD * 2);
+    // (the lane index, pinned here so that the addresses below are computed here and
+    // not hoisted above the tile loop, where they would hold registers through it)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int wr = ln & 31;
+    char* wrow = wl + wr * (HD * 2) + 8 * (ln >> 5);
+    const int wsw = swz16(wr);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * db + 8 * g4 + 4 * hi;
         const bf16x4 v = {(bf16)(dqacc[db][4 * g4] * f.scale), (bf16)(dqacc[db][4 * g4 + 1] * f.scale),
                           (bf16)(dqacc[db][4 * g4 + 2] * f.scale), (bf16)(dqacc[db][4 * g4 + 3] * f.scale)};
-        *reinterpret_cast<bf16x4*>(dqp + d) = v;
+        // columns 32db + 8g4 + 4hi + 0..3 of row r32: logical chunk 4db + g4, half hi
+        *reinterpret_cast<bf16x4*>(wrow + (((4 * db + g4) ^ wsw) << 4)) = v;
       }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own writes, read back below
+    // rows 4k + lane/16 of the wave, chunk lane % 16; a tile never crosses a block of
+    // the row layout, so the rows are one row stride apart
+    const int c = ln & 15, orow0 = qt * BR + wave * 32 + (ln >> 4);
+    bf16* dqp = reinterpret_cast<bf16*>(a.dq) + rows_off(f.lq, orow0, h) + 8 * c;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int rr = 4 * k + (ln >> 4);
+      const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(wl + rr * (HD * 2) + ((c ^ swz16(rr)) << 4));
+      if (orow0 + 4 * k < f.Sq) *reinterpret_cast<bf16x8*>(dqp + 4 * k * f.lq.row_stride) = v8;
     }
   }
 }
