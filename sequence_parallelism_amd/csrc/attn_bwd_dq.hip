@@ -216,6 +216,15 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
     const bf16* Kb = &stage[buf][0];
     const bf16* Vb = &stage[buf][TILE];
     const int ktn = min(kt + BC, last_kt);   // the last tile fetches itself again (unused)
+    // a tile that no row of this wave sees (causal diagonal, document starts) has
+    // P = dS = 0 there: the wave only sends its share of the next tile's DMA
+    // (wave-uniform branch)
+    if (wk.hiex <= kt || wk.lo >= kt + BC) {
+      for (int s = 0; s < 2 * NL; ++s) dma_step(s, ktn, buf ^ 1);
+      wait_vmem();
+      __syncthreads();
+      continue;
+    }
 
     // ---- S^T and dP^T: 64 keys x 32 queries each.  MFMA i: S (even i) or dP (odd i)
     // of key block kb2 = (i/2)%2, d chunk kk = i/4; the next tile's DMA rides along --

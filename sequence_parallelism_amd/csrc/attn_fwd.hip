@@ -181,6 +181,15 @@ __device__ __forceinline__ void attn_fwd_unit(const AttnArgs& a, int n_qtiles, i
     const bf16* Kb = &stage[buf][0];
     const bf16* Vb = &stage[buf][TILE];
     const int ktn = min(kt + BC, last_kt);   // the last tile fetches itself again (unused)
+    // a tile that no row of this wave sees (causal diagonal, document starts) adds
+    // nothing to m, l or O: the wave only sends its share of the next tile's DMA
+    // (wave-uniform branch)
+    if (wk.hiex <= kt || wk.lo >= kt + BC) {
+      for (int s = 0; s < 2 * NL; ++s) dma_step(s, ktn, buf ^ 1);
+      wait_vmem();
+      __syncthreads();
+      continue;
+    }
     // ---- S^T tile: 128 keys x 32 queries (MFMA i: 32-key block i%4, d chunk i/4); the
     // next tile's DMA rides along --------------------------------------------------
     f32x16 sacc[NKB];
