@@ -86,6 +86,33 @@ def test_packed_128k_fwd_bwd(usp):
     check_lse(lse[:, rows].cpu(), ref_l, "lse sampled rows")
 
 
+def test_single_doc_causal_128k_fwd_bwd(usp):
+    """The packed 128K tensors as ONE causal document (position_ids 0..131071): O and
+    LSE at sampled rows, dQ at sampled rows, and dK, dV of the last 128 keys, which
+    only the last 128 rows see (so those rows' contributions are their whole
+    gradient)."""
+    say("single-document causal 128k")
+    q, k, v, do, _, _ = inputs.packed_128k()
+    S = q.shape[0]
+    pos = np.arange(S, dtype=np.int32)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    posd = torch.from_numpy(pos).to(DEV)
+    o, lse = usp.blockattn_fwd(qd, kd, vd, posd)
+    dq, dk, dv = usp.blockattn_bwd(qd, kd, vd, o, lse, dod, posd)
+    torch.cuda.synchronize()
+    args = (f64(q), f64(k), f64(v))
+    rows = sample_rows(S, 24, 3)
+    ref_o, ref_l = oracle.attention_fwd(*args, pos=pos, causal=True, rows=rows)
+    check_o(o[rows].cpu(), ref_o, "o sampled rows")
+    check_lse(lse[:, rows].cpu(), ref_l, "lse sampled rows")
+    rq, _, _ = oracle.attention_bwd(*args, f64(do), pos=pos, causal=True, rows=rows)
+    check_grad(dq[rows].cpu(), rq, "dq sampled rows")
+    tail = np.arange(S - 128, S)
+    _, rk, rv = oracle.attention_bwd(*args, f64(do), pos=pos, causal=True, rows=tail)
+    check_grad(dk[S - 128:].cpu(), rk[S - 128:], "dk last 128 keys")
+    check_grad(dv[S - 128:].cpu(), rv[S - 128:], "dv last 128 keys")
+
+
 def test_ring_256k_blockwise_merge(usp):
     """S = 262144, 2 heads, causal: query block i (16384 rows) attends key blocks
     0..i one call at a time (fp32 partials), merged into an accumulator
