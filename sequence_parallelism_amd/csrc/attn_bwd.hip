@@ -8,7 +8,7 @@
 // Kernels, in stream order:
 //   1. dQ:        attn_bwd_dq.hip, query-stationary, recomputing S and dP (no atomics);
 //                 it forms D_i from the dO and O rows it holds and writes the row
-//                 scalars of the dK/dV kernel (-lse log2 e, -D, the visible keys);
+//                 scalars of the dK/dV kernel (lse log2 e, -D, the visible keys);
 //   2. dK, dV:    a workgroup owns 128 keys of one key/value head (32 per wave; K
 //                 and V of the lane's key are B operands in registers) and walks the
 //                 128-row query tiles that can see the block, for every query head of
@@ -85,7 +85,7 @@ static_assert(sdp_order(4) == 8 && sdp_order(5) == 4 && sdp_order(11) == 7 && sd
 // chunk c of its key block's items (a.kv_split chunks) and writes its partial dK^T,
 // dV^T sums for the combine pass.
 typedef bf16 StageBuf[2][2 * BQ * HD];   // per buffer: Q [128 rows][128], dO [128][128] (swz16)
-typedef uint32_t ScalBuf[4][2][BQ];      // per buffer: -lse log2(e), -D, klo, khi per row
+typedef uint32_t ScalBuf[4][2][BQ];      // per buffer: lse log2(e), -D, klo, khi per row
 template <bool SPLIT, typename Fetch>
 __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles, int unit, StageBuf& stage,
                                               ScalBuf& scal_s, Fetch&& fetch_unit, int& next_unit) {
@@ -182,7 +182,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
     uint32_t lim;          // rows past Sq are clamped to the last row (the mask zeroes them)
     const uint32_t* sc;    // this wave's row-scalar plane at row q0
   };
-  // wave w stages row-scalar plane w of the item: -lse log2(e) and -D of its head,
+  // wave w stages row-scalar plane w of the item: lse log2(e) and -D of its head,
   // klo and khi of its rows
   const uint32_t* const sc_wave = a.rs + (int64_t)(wave < 2 ? wave * f.Hq : 2 * f.Hq + wave - 2) * a.rs_ld;
   const int64_t sc_hstep = wave < 2 ? a.rs_ld : 0;
@@ -271,28 +271,6 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
     constexpr int qb = decltype(QB)::v, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
     e4[qb % 2][g4] = *reinterpret_cast<const f32x4*>(&scal_s[1][b][q + 4 * hi]);
   };
-  // -lse2 of rows 32qb + 8g4 + 4hi + 0..3 (the S accumulators' start), from buffer b,
-  // read five to eight steps before block qb's first S step (block 0's at the end of
-  // the item before); in a boundary item the row's hidden pairs get -inf, so that P and
-  // dS vanish there (mask_rows, right after the read: a boundary item waits for it)
-  f32x4 l4[2][4];
-  auto mask_rows = [&](auto QB, auto G4, int b) {
-    constexpr int qb = decltype(QB)::v, x = qb % 2, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
-    const int4 lov = *reinterpret_cast<const int4*>(&scal_s[2][b][q + 4 * hi]);
-    const int4 hiv = *reinterpret_cast<const int4*>(&scal_s[3][b][q + 4 * hi]);
-    const int loa[4] = {lov.x, lov.y, lov.z, lov.w};
-    const int hia[4] = {hiv.x, hiv.y, hiv.z, hiv.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool vis = (kl >= loa[e]) & (kl < hia[e]) & key_ok;
-      l4[x][g4][e] = vis ? l4[x][g4][e] : -INFINITY;
-    }
-  };
-  auto load_rows = [&](auto QB, auto G4, int b, auto mask_tag) {
-    constexpr int qb = decltype(QB)::v, x = qb % 2, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
-    l4[x][g4] = *reinterpret_cast<const f32x4*>(&scal_s[0][b][q + 4 * hi]);
-    if constexpr (decltype(mask_tag)::v != 0) mask_rows(QB, G4, b);
-  };
   bf16x8 ops[2 * PF];   // operand reads in flight (a ring of 2 PF), carried from item to item
 
   // item 0 is staged before the loop; nx: where item it+1 comes from (used by item
@@ -326,46 +304,36 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
     __syncthreads();
     unroll<PF>([&](auto I) { ops[decltype(I)::v] = op_at(I, 0); });
     unroll<4>([&](auto G4) { load_nd(IC<0>{}, G4, 0); });
-    unroll<4>([&](auto G4) { load_rows(IC<0>{}, G4, 0, IC<0>{}); });
   }
   // K and V consumed here, after item 0's DMA (with which they were in flight), so that
   // the compiler waits for them once, now, and not inside the item loop (where its wait
   // would also cover the tile DMA in flight)
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) asm volatile("" :: "v"(kf[kk]), "v"(vf[kk]));
-  // K carries scale log2(e), so that the S accumulators hold the exponent of P (their
-  // start is -lse2); the product is rounded to bf16 like K itself
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) kf[kk][e] = (bf16)((float)kf[kk][e] * sl2);
-  }
 
-  // one item; MASK: a boundary item, whose hidden (row, key) pairs start their S
-  // accumulation at -inf so that P and dS vanish there
+  // one item; MASK: a boundary item, whose hidden (row, key) pairs get the row
+  // log-sum-exp +inf so that P and dS vanish there
   auto run_item = [&](auto mask_tag, int it) {
     constexpr bool MASK = decltype(mask_tag)::v != 0;
     const int buf = (it - it0) & 1;
     // every wave is done with item it-1, which read buffer buf ^ 1: it can be refilled
     // (item it itself was published halfway through item it-1's last slot)
     __syncthreads();
-    if constexpr (MASK) unroll<4>([&](auto G4) { mask_rows(IC<0>{}, G4, buf); });
     {
       f32x16 sacc[2], dpacc[2];
+      f32x4 l4[2][4];
       bf16x8 pb[2][2], sb[2][2];
       uint32_t vq = 0;
       const uint32_t dbase = dma_base(buf ^ 1);   // item it+1 goes to the other buffer
 
       // P and dS of element e of 32-row block qb (row 32qb + 8(e/4) + 4hi + e%4), in two
       // stages one step apart so that no instruction waits on the exponential:
-      //   A: P = 2^(s sl2 - lse2), the accumulator already holding the exponent (K
-      //      carries sl2, the accumulation started at -lse2);
-      //   B: dS = P (dP - D), and P, dS packed to bf16 pairs
+      //   A: P = 2^(s sl2 - lse2);   B: dS = P (dP - D), and P, dS packed to bf16 pairs
       float pv[2][16];
       float ds_prev = 0.f;
       auto soft_a = [&](auto QB, auto E) {
         constexpr int x = decltype(QB)::v % 2, e = decltype(E)::v;
-        pv[x][e] = __builtin_amdgcn_exp2f(sacc[x][e]);
+        pv[x][e] = __builtin_amdgcn_exp2f(fmaf(sacc[x][e], sl2, -l4[x][e >> 2][e & 3]));
       };
       auto soft_b = [&](auto QB, auto E) {
         constexpr int x = decltype(QB)::v % 2, e = decltype(E)::v;
@@ -377,6 +345,22 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
           sb[x][e >> 3][e & 7] = (bf16)ds;
         } else {
           ds_prev = ds;
+        }
+      };
+      // row scalars of rows 32qb + 8g4 + 4hi + 0..3, read four steps before first use
+      auto load_rows = [&](auto QB, auto G4) {
+        constexpr int qb = decltype(QB)::v, x = qb % 2, g4 = decltype(G4)::v, q = 32 * qb + 8 * g4;
+        l4[x][g4] = *reinterpret_cast<const f32x4*>(&scal_s[0][buf][q + 4 * hi]);
+        if constexpr (MASK) {
+          const int4 lov = *reinterpret_cast<const int4*>(&scal_s[2][buf][q + 4 * hi]);
+          const int4 hiv = *reinterpret_cast<const int4*>(&scal_s[3][buf][q + 4 * hi]);
+          const int loa[4] = {lov.x, lov.y, lov.z, lov.w};
+          const int hia[4] = {hiv.x, hiv.y, hiv.z, hiv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool vis = (kl >= loa[e]) & (kl < hia[e]) & key_ok;
+            l4[x][g4][e] = vis ? l4[x][g4][e] : INFINITY;
+          }
         }
       };
       mfma_pipeline_carry2<PF, 16 * 2 * NQB>(
@@ -399,13 +383,8 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
                 } else {
                   dpacc[x] = mfma32(op, vf[kk], dpacc[x]);
                 }
-              } else if constexpr (kk == 0) {   // S starts from -lse2 of the element's row
-                f32x16 c;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) c[e] = l4[x][e >> 2][e & 3];
-                sacc[x] = mfma32(op, kf[0], c);
               } else {
-                sacc[x] = mfma32(op, kf[kk], sacc[x]);
+                sacc[x] = mfma32(op, kf[kk], kk == 0 ? f32x16{} : sacc[x]);
               }
             } else {
               // k-slot s of lane half hi in row chunk c is row 16c + 8(s/4) + 4hi + s%4,
@@ -417,11 +396,13 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
           },
           [&](auto I) {   // work hidden behind MFMA i
             constexpr int i = decltype(I)::v, slot = i / 16, j = i % 16;
-            // -lse2 of block b before its S slot, after block b-2's S has used the same
-            // registers (block 0's comes at the end of the item before)
-            if constexpr (i >= 6 && i < 10) load_rows(IC<1>{}, IC<i - 6>{}, buf, mask_tag);
-            if constexpr (i >= 38 && i < 42) load_rows(IC<2>{}, IC<i - 38>{}, buf, mask_tag);
-            if constexpr (i >= 70 && i < 74) load_rows(IC<3>{}, IC<i - 70>{}, buf, mask_tag);
+            // block b's softmax runs in slot sm_slot(b); its rows of group g4 are read four
+            // steps before their first use
+            unroll<NQB>([&](auto B) {
+              constexpr int qb = decltype(B)::v, s0 = 16 * sm_slot(qb);
+              if constexpr (i >= s0 - 4 && i <= s0 + 8 && (i - s0) % 4 == 0)
+                load_rows(IC<qb>{}, IC<(i - s0 + 4) / 4>{});
+            });
             // -D of block b before its S slot, after block b-2 has used the same registers
             if constexpr (i >= 8 && i < 12) load_nd(IC<1>{}, IC<i - 8>{}, buf);
             if constexpr (i >= 41 && i < 45) load_nd(IC<2>{}, IC<i - 41>{}, buf);
@@ -450,10 +431,7 @@ __device__ __forceinline__ void attn_bwd_unit(const AttnBwdArgs& a, int n_qtiles
               store_scalars(buf ^ 1);
               __syncthreads();
             }
-            if constexpr (i >= 121 && i < 125) {
-              load_nd(IC<0>{}, IC<i - 121>{}, buf ^ 1);
-              load_rows(IC<0>{}, IC<i - 121>{}, buf ^ 1, IC<0>{});   // masked by item it+1 itself
-            }
+            if constexpr (i >= 121 && i < 125) load_nd(IC<0>{}, IC<i - 121>{}, buf ^ 1);
             // block b's softmax: stage A of element j and stage B of element j-1 in slot
             // sm_slot(b), stage B of element 15 at the first step of the next slot
             unroll<NQB>([&](auto B) {

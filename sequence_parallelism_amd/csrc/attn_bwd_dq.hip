@@ -174,12 +174,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(AttnBwdArgs a, int
   }
   const float lse2 = row_ok ? (l_raw == -INFINITY ? INFINITY : l_raw * USP_LOG2E) : INFINITY;
   // the dK/dV kernel's row scalars (it runs after this kernel), once per (row, head):
-  // -lse log2(e), -D and, for head 0, the row's visible keys; rows past Sq up to the
+  // lse log2(e), -D and, for head 0, the row's visible keys; rows past Sq up to the
   // planes' padding (to whole 128-row items of that kernel, inside this kernel's
   // 128- or 256-row tiles) get 0, 0 and the empty range [KBIG, -KBIG)
   if (hi == 0 && chunk == 0 && row < a.rs_ld) {
     const int64_t ld = a.rs_ld;
-    reinterpret_cast<float*>(a.rs)[(int64_t)h * ld + row] = row_ok ? -(l_raw * USP_LOG2E) : 0.f;
+    reinterpret_cast<float*>(a.rs)[(int64_t)h * ld + row] = row_ok ? l_raw * USP_LOG2E : 0.f;
     reinterpret_cast<float*>(a.rs)[((int64_t)f.Hq + h) * ld + row] = row_ok ? -dlt : 0.f;
     if (h == 0) {
       int* klop = reinterpret_cast<int*>(a.rs) + 2 * (int64_t)f.Hq * ld + row;

@@ -209,6 +209,26 @@ def test_fwd_large_logits(usp):
     check_lse(lse, ref_l, "lse")
 
 
+def test_bwd_large_logits(usp):
+    """Gradients with scores of magnitude ~100s (q scaled by 30, as in the forward's
+    large-logit test): P is sharply peaked, so an error in a score's exponent shows
+    directly in P, dS and the gradients."""
+    say("bwd large logits")
+    q, k, v, do, pos = inputs.attention_case(384, 2, 2, 128, seed=9, lengths=[200, 184])
+    q = (q.float() * 30).to(torch.bfloat16)
+    args = (f64(q), f64(k), f64(v))
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    posd = torch.from_numpy(pos).to(DEV)
+    o, lse = usp.blockattn_fwd(qd, kd, vd, posd)
+    dq, dk, dv = usp.blockattn_bwd(qd, kd, vd, o, lse, dod, posd)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd(*args, f64(do), pos=pos, causal=True)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        say("  ", name, "max |err| / max |ref|",
+            float(np.abs(f64(got) - ref).max() / max(np.abs(ref).max(), 1e-3)))
+        check_grad(got.cpu(), ref, name)
+
+
 def test_fwd_causal_4k_full(usp):
     """Single-device causal attention, [4096][8][128] bf16, every output."""
     say("fwd causal 4k")
