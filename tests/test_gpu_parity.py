@@ -229,6 +229,32 @@ def test_bwd_large_logits(usp):
         check_grad(got.cpu(), ref, name)
 
 
+def test_large_logits_long_gqa(usp):
+    """Large logits (q scaled by 30) on the 8-wave kernels: 32768 rows in two documents,
+    4 query heads on 1 key/value head; every output against the oracle.  (The gradient
+    tolerance is relative to the max norm of the whole tensor: keys seen by few rows,
+    under attention this peaked, carry the bf16 rounding of the O the backward receives,
+    which enters D = <dO, O>, at a larger share of their own small gradients.)"""
+    say("large logits, 32k gqa")
+    S = 32768
+    q, k, v, do, pos = inputs.attention_case(S, 4, 1, 128, seed=11, lengths=[20000, 12768])
+    q = (q.float() * 30).to(torch.bfloat16)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    posd = torch.from_numpy(pos).to(DEV)
+    o, lse = usp.blockattn_fwd(qd, kd, vd, posd)
+    dq, dk, dv = usp.blockattn_bwd(qd, kd, vd, o, lse, dod, posd)
+    torch.cuda.synchronize()
+    args = (f64(q), f64(k), f64(v))
+    ref_o, ref_l = oracle.attention_fwd(*args, pos=pos, causal=True)
+    check_o(o.cpu(), ref_o, "o")
+    check_lse(lse.cpu(), ref_l, "lse")
+    rq, rk, rv = oracle.attention_bwd(*args, f64(do), pos=pos, causal=True)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        say("  ", name, "max |err| / max |ref|",
+            float(np.abs(f64(got) - ref).max() / max(np.abs(ref).max(), 1e-3)))
+        check_grad(got.cpu(), ref, name)
+
+
 def test_fwd_causal_4k_full(usp):
     """Single-device causal attention, [4096][8][128] bf16, every output."""
     say("fwd causal 4k")
